@@ -1,0 +1,170 @@
+"""Explicit n x n masked-softmax attention in float64 (the oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the product
+path may import this module.
+
+What is computed, for one (batch, head) with window ``w`` and dilation ``delta``
+(Longformer summary page, section 3-1):
+
+* band(i, j)  <=>  |i - j| <= (w/2) * delta  and  (i - j) mod delta == 0.
+  "Sliding Window": a token attends to w/2 tokens on each side.
+  "Dilated Sliding Window": the window keeps its size (its number of keys)
+  while gaps of ``delta`` widen the span it covers.
+* caus(i, j)  <=>  not causal  or  j <= i
+  (section 7: the decoder's self-attention looks left only).
+* A non-global row i attends to  A(i) = {j : (band(i, j) or j in G) and
+  caus(i, j)}  with the regular Q, K, V ("Global Attention": every token
+  attends to the global tokens; a global key already in the band counts once).
+* A global row g attends to every j with caus(g, j), using the separate global
+  projections Qg, Kg, Vg ("Linear Projections for Global Attention").
+* O_i = sum_{j in A(i)} softmax_j(s * q_i . k_j) v_j  with s = 1/sqrt(d), and
+  LSE_i = ln sum_{j in A(i)} exp(s * q_i . k_j).
+
+Readings taken where the page is silent or garbled:
+
+* R1  the window is +-w/2 keys inclusive, so an interior row has w+1 keys;
+      w must be even.
+* R2  dilation puts keys at i +- k*delta for k <= w/2 (span w*delta, key count
+      unchanged), which is what "keeps the compute, widens the receptive
+      field" means; the printed O(n*w*d) contradicts the same sentence.
+* R3  causal keeps the same band on the left: keys i - k*delta, 0 <= k <= w/2.
+* R4  the softmax scale is 1/sqrt(d) (the page writes no formula).
+* R5  global rows use Qg, Kg, Vg over all positions; global columns use the
+      regular K[G], V[G], so each row is one softmax over one projection set.
+* R6  a global key inside a row's band counts once (set union).
+* R7  causal applies to global rows and columns too.
+* R8  one G shared by every batch item and head; dilation applies to the band
+      only.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["band_mask", "global_row_mask", "allowed_mask", "attention"]
+
+
+def band_mask(rows, n, window, dilation, causal):
+    """Boolean [len(rows), n]: band(i, j) and caus(i, j) for i in ``rows``.
+
+    Section 3-1 "Sliding Window" / "Dilated Sliding Window" (readings R1-R3).
+    """
+    if window < 0 or window % 2:
+        raise ValueError("window must be even and >= 0")
+    if dilation < 1:
+        raise ValueError("dilation must be >= 1")
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(n, dtype=np.int64)[None, :]
+    diff = i - j
+    m = (np.abs(diff) <= (window // 2) * dilation) & (diff % dilation == 0)
+    if causal:
+        m &= j <= i
+    return m
+
+
+def global_row_mask(rows, n, causal):
+    """Boolean [len(rows), n] for global rows: every key, left only if causal.
+
+    Section 3-1 "Global Attention" (a global token attends to all tokens), R7.
+    """
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(n, dtype=np.int64)[None, :]
+    m = np.ones((i.shape[0], n), dtype=bool)
+    if causal:
+        m &= j <= i
+    return m
+
+
+def allowed_mask(rows, n, window, dilation, causal, global_idx):
+    """Boolean [len(rows), n]: the key set A(i) of every row in ``rows``.
+
+    Non-global rows: (band or j in G) and caus (R5-R7). Global rows: every
+    key allowed by caus. Section 3-1, all four bullets.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    g = np.zeros(n, dtype=bool)
+    g[np.asarray(global_idx, dtype=np.int64)] = True
+    m = band_mask(rows, n, window, dilation, False)
+    m |= g[None, :]
+    if causal:
+        m &= np.arange(n)[None, :] <= rows[:, None]
+    rg = g[rows]
+    if rg.any():
+        m[rg] = global_row_mask(rows[rg], n, causal)
+    return m
+
+
+def _masked_softmax_rows(qr, k, v, mask, scale):
+    """softmax(scale * qr k^T restricted to mask) v, and its log-sum-exp.
+
+    Plain definition of attention over an explicit key set: scores, -inf
+    outside the set, subtract the row max, exponentiate, normalise, multiply.
+    """
+    s = scale * (qr @ k.T)
+    s = np.where(mask, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    den = p.sum(axis=1, keepdims=True)
+    o = (p @ v) / den
+    lse = mx[:, 0] + np.log(den[:, 0])
+    return o, lse
+
+
+def attention(q, k, v, qg=None, kg=None, vg=None, *, window, dilation,
+              causal=False, global_idx=(), rows=None, row_block=1024):
+    """Oracle forward: O [B,H,R,d] and LSE [B,H,R] in float64.
+
+    ``q, k, v`` (and ``qg, kg, vg`` when G is not empty) are [B,H,n,d] arrays;
+    they are upcast to float64 exactly. ``window`` and ``dilation`` are per
+    head (sequences of length H) or scalars. ``rows`` selects which rows to
+    compute (default: all n); R = len(rows). ``global_idx`` may be unsorted
+    but must not repeat.
+
+    Each row block builds the explicit [rows x n] mask and evaluates the
+    masked softmax directly (section 3-1; readings R1-R8 above).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, n, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B,H,n,d] shape")
+    gl = np.asarray(global_idx, dtype=np.int64).reshape(-1)
+    if gl.size:
+        if len(np.unique(gl)) != gl.size:
+            raise ValueError("global_idx repeats an index")
+        if gl.min() < 0 or gl.max() >= n:
+            raise ValueError("global_idx out of range")
+        qg = np.asarray(qg, dtype=np.float64)
+        kg = np.asarray(kg, dtype=np.float64)
+        vg = np.asarray(vg, dtype=np.float64)
+        for t in (qg, kg, vg):
+            if t.shape != q.shape:
+                raise ValueError("qg, kg, vg must have q's shape")
+    win = np.broadcast_to(np.asarray(window, dtype=np.int64), (H,))
+    dil = np.broadcast_to(np.asarray(dilation, dtype=np.int64), (H,))
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    isg = np.zeros(n, dtype=bool)
+    isg[gl] = True
+    scale = 1.0 / np.sqrt(d)
+
+    R = rows.size
+    o = np.zeros((B, H, R, d), dtype=np.float64)
+    lse = np.zeros((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for s0 in range(0, R, row_block):
+                rb = rows[s0:s0 + row_block]
+                mask = allowed_mask(rb, n, int(win[h]), int(dil[h]), causal, gl)
+                reg = ~isg[rb]
+                if reg.any():
+                    oo, ll = _masked_softmax_rows(q[b, h, rb[reg]], k[b, h],
+                                                  v[b, h], mask[reg], scale)
+                    o[b, h, s0 + np.nonzero(reg)[0]] = oo
+                    lse[b, h, s0 + np.nonzero(reg)[0]] = ll
+                if (~reg).any():
+                    oo, ll = _masked_softmax_rows(qg[b, h, rb[~reg]], kg[b, h],
+                                                  vg[b, h], mask[~reg], scale)
+                    o[b, h, s0 + np.nonzero(~reg)[0]] = oo
+                    lse[b, h, s0 + np.nonzero(~reg)[0]] = ll
+    return o, lse

@@ -1,0 +1,136 @@
+"""Workload shapes and seeded synthetic inputs.
+
+This module holds no arithmetic of the attention method: it only names shapes
+and draws random tensors. Both the HIP path (tests, bench) and the float64
+oracle consume what it produces, so it is the one module they share.
+
+Shapes stand in for the workloads on the Longformer summary page: the
+Longformer-base encoder shape, the autoregressive character-LM shapes of
+section 4 (windows per layer, dilation on two heads, staged sequence length up
+to 23,040), the QA shape of section 3-1 "Global Attention" (question tokens as
+globals) and the LED encoder of section 7 (16K tokens, window 1024, one global
+token). No dataset is read; every tensor is drawn from a seeded generator.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "DTYPES"]
+
+DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    n: int
+    d: int
+    window: tuple
+    dilation: tuple
+    causal: bool
+    global_idx: tuple = field(default=())
+    dtype: str = "bf16"
+    scale: float = 0.125
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    def with_(self, **kw):
+        return replace(self, **kw)
+
+
+def _per_head(h, v, over=None):
+    t = [v] * h
+    for idx, val in (over or {}).items():
+        t[idx] = val
+    return tuple(t)
+
+
+WORKLOADS = {
+    # single head, fp32, symmetric +-32 window; the small case the oracle
+    # finishes in well under a second
+    "single_head_fp32_n512_w64": Workload(
+        "single_head_fp32_n512_w64", 1, 1, 512, 64, (64,), (1,), False, (),
+        "fp32", 8 ** -0.5),
+    # Longformer-base-shaped encoder with one global token (position 0)
+    "encoder_b2_h12_n4096_w512_g1": Workload(
+        "encoder_b2_h12_n4096_w512_g1", 2, 12, 4096, 64, _per_head(12, 512),
+        _per_head(12, 1), False, (0,)),
+    # the same encoder with no global token: the band pass alone
+    "encoder_b2_h12_n4096_w512": Workload(
+        "encoder_b2_h12_n4096_w512", 2, 12, 4096, 64, _per_head(12, 512),
+        _per_head(12, 1), False, ()),
+    # autoregressive char-LM phase: causal, dilation 2 on heads 10-11
+    "arlm_b1_h12_n8192_w512_causal_dil2": Workload(
+        "arlm_b1_h12_n8192_w512_causal_dil2", 1, 12, 8192, 64,
+        _per_head(12, 512), _per_head(12, 1, {10: 2, 11: 2}), True, ()),
+    # autoregressive char-LM final stage: n = 23040, dilation 4 on heads 6-7
+    "arlm_b1_h8_n23040_w1024_causal_dil4": Workload(
+        "arlm_b1_h8_n23040_w1024_causal_dil4", 1, 8, 23040, 64,
+        _per_head(8, 1024), _per_head(8, 1, {6: 4, 7: 4}), True, ()),
+    # QA-style: 64 global tokens (positions 0-63)
+    "qa_b4_h12_n4096_w512_g64": Workload(
+        "qa_b4_h12_n4096_w512_g64", 4, 12, 4096, 64, _per_head(12, 512),
+        _per_head(12, 1), False, tuple(range(64))),
+    # LED encoder: 16K tokens, window 1024, global attention on the first token
+    "led_b1_h12_n16384_w1024_g1": Workload(
+        "led_b1_h12_n16384_w1024_g1", 1, 12, 16384, 64, _per_head(12, 1024),
+        _per_head(12, 1), False, (0,)),
+}
+
+
+def _draw(gen, shape, scale, kind, role):
+    if kind == "sharp" and role == "v":
+        x = torch.rand(shape, generator=gen, dtype=torch.float32) * 2.0 - 1.0
+    elif kind == "sharp":
+        x = torch.randn(shape, generator=gen, dtype=torch.float32) * 2.0
+    else:
+        x = torch.randn(shape, generator=gen, dtype=torch.float32) * scale
+    return x
+
+
+def make_inputs(wl: Workload, seed: int, kind: str = "normal"):
+    """Seeded CPU tensors q, k, v, qg, kg, vg ([B,H,n,d], the workload dtype).
+
+    Draw order: q, k, v, then qg, kg, vg when the workload has global tokens
+    (those three are None otherwise). Values are drawn in float32 and rounded
+    to nearest-even into the workload dtype.
+
+    ``kind``:
+      * "normal": i.i.d. N(0,1) * scale;
+      * "sharp":  q, k ~ N(0,1) * 2 and v ~ U(-1, 1), so softmax rows are
+        peaked and a wrong key set moves the output far beyond tolerance;
+      * "dedup":  "normal", plus a direction u shared by every query and by the
+        regular keys at the global positions, and one-hot values (8 e_j) at
+        those positions: each global key then takes a large share of every
+        row, so counting a global key twice shows up in the output.
+    """
+    if kind not in ("normal", "sharp", "dedup"):
+        raise ValueError(kind)
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    shape = (wl.batch, wl.heads, wl.n, wl.d)
+    out = {}
+    roles = ["q", "k", "v"] + (["qg", "kg", "vg"] if wl.global_idx else [])
+    for r in roles:
+        out[r] = _draw(gen, shape, wl.scale, kind,
+                       "v" if r in ("v", "vg") else "qk")
+    if kind == "dedup" and wl.global_idx:
+        u = torch.randn((wl.d,), generator=gen, dtype=torch.float32)
+        u = u / u.norm() * wl.d ** 0.5
+        gi = torch.tensor(wl.global_idx, dtype=torch.long)
+        out["q"] = out["q"] + 0.25 * u
+        out["k"][:, :, gi, :] = 3.0 * u
+        vv = torch.zeros((len(wl.global_idx), wl.d), dtype=torch.float32)
+        vv[torch.arange(len(wl.global_idx)), gi % wl.d] = 8.0
+        out["v"][:, :, gi, :] = vv
+    for r in list(out):
+        out[r] = out[r].to(wl.torch_dtype).contiguous()
+    for r in ("qg", "kg", "vg"):
+        out.setdefault(r, None)
+    return out
