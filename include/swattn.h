@@ -1,0 +1,129 @@
+/*
+ * swattn.h -- C ABI of the banded sliding-window attention library for AMD
+ * MI355X (gfx950).
+ *
+ * The operation is Longformer-style self-attention as the Longformer summary
+ * page (velog.io/@lainshower/Longformer) describes it in section 3-1
+ * "Attention Pattern":
+ *   - "Sliding Window": token i attends to w/2 tokens on each side;
+ *   - "Dilated Sliding Window": the window keeps its w+1 keys, spaced by a
+ *     per-head dilation, so its span grows to w*dilation;
+ *   - "Global Attention": a small set G of tokens attends to every token and
+ *     is attended by every token;
+ *   - "Linear Projections for Global Attention": the rows of G are computed
+ *     from separate projections Qg, Kg, Vg;
+ * and section 7 "Longformer-Encoder-Decoder" for the optional left-only
+ * (causal) mask.
+ *
+ * Precisely, for head h with window w_h (even) and dilation d_h, and the
+ * softmax scale s = 1/sqrt(d):
+ *   band(i,j)  <=>  j = i + k*d_h  for an integer k in [-w_h/2, R_h],
+ *                   R_h = 0 when causal, w_h/2 otherwise;
+ *   row i not in G:  keys A(i) = band(i) U {g in G : (not causal) or g <= i},
+ *                    each key counted once, projections Q, K, V;
+ *   row g in G:      keys {j : (not causal) or j <= g}, projections Qg, Kg, Vg;
+ *   O_i   = sum_{j in A(i)} softmax_j(s q_i.k_j) v_j,
+ *   LSE_i = ln sum_{j in A(i)} exp(s q_i.k_j)   (natural log, fp32).
+ *
+ * Threading: a plan may be used from any host thread, but not by two
+ * in-flight forwards at once (they share the plan's device workspace).
+ * No C++ exception crosses this interface.
+ */
+#ifndef SWATTN_H
+#define SWATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define SWATTN_OK 0
+#define SWATTN_ERR_INVALID_ARG 1 /* a parameter is out of its documented range */
+#define SWATTN_ERR_UNSUPPORTED 2 /* valid, but not implemented (e.g. d != 64) */
+#define SWATTN_ERR_HIP 3         /* the HIP runtime reported an error */
+#define SWATTN_ERR_ALIGNMENT 4   /* a device pointer is not 16-byte aligned */
+
+/* Element types of Q, K, V, Qg, Kg, Vg and O. */
+#define SWATTN_BF16 0 /* bfloat16 in and out, fp32 accumulation */
+#define SWATTN_FP32 1 /* fp32 in and out, fp32 accumulation */
+
+typedef struct swattn_params {
+  int32_t batch;               /* B >= 1 */
+  int32_t heads;               /* H >= 1 */
+  int32_t n;                   /* sequence length, 1 <= n <= 2^24 */
+  int32_t d;                   /* head dimension; only 64 is supported */
+  const int32_t* window;       /* host [H]: w_h, even, 0 <= w_h (any size; clipped at the ends) */
+  const int32_t* dilation;     /* host [H]: d_h >= 1 */
+  int32_t causal;              /* 0 or 1: left-only mask on band, global rows and global columns */
+  const int32_t* global_idx;   /* host [n_global]: positions of G, each in [0, n), no repeats, any order */
+  int32_t n_global;            /* 0 <= |G| <= n; global_idx may be NULL when 0 */
+  int32_t dtype;               /* SWATTN_BF16 or SWATTN_FP32 */
+} swattn_params;
+
+typedef struct swattn_plan swattn_plan;
+
+/*
+ * Validate the parameters and build a plan: per-head (left, right, dilation)
+ * table, the residue-class tile schedule of the band, the sorted device copy
+ * of G, and the device workspace for the global-row pass. Every host array is
+ * copied; the caller may free them when this returns. Uses the current HIP
+ * device; the plan may only be used with streams of that device.
+ * On success *out receives the plan; on failure *out is untouched.
+ * Errors: INVALID_ARG (null pointers, ranges, odd window, dilation < 1,
+ * repeated or out-of-range global index), UNSUPPORTED (d != 64, unknown
+ * dtype), HIP (device allocation or copy failed; see swattn_last_error()).
+ */
+int swattn_create(const swattn_params* p, swattn_plan** out);
+
+/*
+ * Enqueue one forward pass on `stream` (a hipStream_t; NULL = the default
+ * stream) and return without waiting.
+ *   q, k, v     device, [B, H, n, d] contiguous (d fastest), plan dtype;
+ *   qg, kg, vg  device, same shape and dtype: the separate global projections
+ *               (only rows G of qg are read; kg, vg are read in full). They
+ *               must be NULL exactly when n_global == 0;
+ *   o           device, [B, H, n, d] plan dtype, written in full; must not
+ *               overlap any input;
+ *   lse         device fp32 [B, H, n] or NULL to skip.
+ * All device pointers must be 16-byte aligned (else ALIGNMENT) and stay
+ * valid until the stream reaches the enqueued work. The caller owns every
+ * buffer; forward allocates nothing. Errors: INVALID_ARG (null plan or
+ * tensor, NULL-ness of qg/kg/vg not matching n_global, o overlapping an
+ * input), ALIGNMENT, HIP (launch failure; see swattn_last_error()).
+ */
+int swattn_forward(swattn_plan* plan, const void* q, const void* k,
+                   const void* v, const void* qg, const void* kg,
+                   const void* vg, void* o, float* lse, void* stream);
+
+/*
+ * Free the plan and its device memory. NULL is a no-op. The caller must make
+ * sure no enqueued forward still uses the plan (e.g. synchronise its stream).
+ */
+int swattn_destroy(swattn_plan* plan);
+
+/*
+ * Measurement hooks (not part of the computation). With timing enabled, each
+ * forward records HIP events on its stream around the band kernel and around
+ * the global-row pass (partial + merge); up to 4096 forwards are kept.
+ * swattn_kernel_times() waits for the recorded events, returns the average
+ * duration in milliseconds of each phase over the recorded forwards and the
+ * number of forwards averaged, then clears the record. Enabling creates the
+ * events (host objects); disabling destroys them. Errors: INVALID_ARG (NULL
+ * plan or outputs), HIP.
+ */
+int swattn_set_timing(swattn_plan* plan, int enable);
+int swattn_kernel_times(swattn_plan* plan, float* band_ms, float* global_ms, int* count);
+
+/* Static, human-readable name of a status code. */
+const char* swattn_status_string(int status);
+
+/* Message of the last error raised on this host thread ("" when none). */
+const char* swattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H */

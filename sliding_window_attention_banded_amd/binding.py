@@ -1,0 +1,184 @@
+"""ctypes binding of libswattn.so (argument marshalling only).
+
+Every step of the forward pass runs in the HIP library; this module checks
+tensor shapes and dtypes, hands raw device pointers and the current HIP
+stream to the C ABI, and turns status codes into exceptions. PyTorch is used
+for device memory and streams only. There is no fallback: if the library is
+missing, creating a Plan raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["Plan", "SwattnError", "library_path", "load_library", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIGNMENT = range(5)
+BF16, FP32 = 0, 1
+EXPORTS = ("swattn_create", "swattn_forward", "swattn_destroy",
+           "swattn_set_timing", "swattn_kernel_times",
+           "swattn_status_string", "swattn_last_error")
+
+
+class SwattnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("window", ctypes.POINTER(ctypes.c_int32)),
+                ("dilation", ctypes.POINTER(ctypes.c_int32)),
+                ("causal", ctypes.c_int32),
+                ("global_idx", ctypes.POINTER(ctypes.c_int32)),
+                ("n_global", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def library_path():
+    return os.environ.get("SWATTN_LIB", os.path.join(_HERE, "libswattn.so"))
+
+
+_lib = None
+
+
+def load_library():
+    """Load libswattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise SwattnError(ERR_HIP, f"{path} is missing: build it with "
+                          "`python -m sliding_window_attention_banded_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.swattn_create.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(vp)]
+    lib.swattn_create.restype = ctypes.c_int
+    lib.swattn_forward.argtypes = [vp] * 8 + [vp, vp]
+    lib.swattn_forward.restype = ctypes.c_int
+    lib.swattn_destroy.argtypes = [vp]
+    lib.swattn_destroy.restype = ctypes.c_int
+    lib.swattn_set_timing.argtypes = [vp, ctypes.c_int]
+    lib.swattn_set_timing.restype = ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.swattn_kernel_times.argtypes = [vp, fp, fp, ctypes.POINTER(ctypes.c_int)]
+    lib.swattn_kernel_times.restype = ctypes.c_int
+    lib.swattn_status_string.argtypes = [ctypes.c_int]
+    lib.swattn_status_string.restype = ctypes.c_char_p
+    lib.swattn_last_error.argtypes = []
+    lib.swattn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(lib, status, what):
+    if status != OK:
+        name = lib.swattn_status_string(status).decode()
+        msg = lib.swattn_last_error().decode()
+        raise SwattnError(status, f"{what}: {name}: {msg}")
+
+
+_DT = {torch.bfloat16: BF16, torch.float32: FP32}
+
+
+class Plan:
+    """A configured banded-attention forward: ``Plan(...).forward(q, k, v)``.
+
+    ``window`` and ``dilation`` are per head (a scalar is broadcast);
+    ``global_idx`` lists the global-token positions shared by all batch items
+    and heads. Tensors are [B, H, n, 64] contiguous CUDA tensors in ``dtype``.
+    """
+
+    def __init__(self, batch, heads, n, d=64, window=512, dilation=1,
+                 causal=False, global_idx=(), dtype=torch.bfloat16):
+        self._lib = load_library()
+        if dtype not in _DT:
+            raise SwattnError(ERR_UNSUPPORTED, f"dtype {dtype} not supported")
+        win = [int(window)] * heads if isinstance(window, int) else [int(x) for x in window]
+        dil = [int(dilation)] * heads if isinstance(dilation, int) else [int(x) for x in dilation]
+        if len(win) != heads or len(dil) != heads:
+            raise SwattnError(ERR_INVALID_ARG, "window/dilation need one entry per head")
+        gl = [int(x) for x in global_idx]
+        self.batch, self.heads, self.n, self.d = batch, heads, n, d
+        self.window, self.dilation, self.causal = tuple(win), tuple(dil), bool(causal)
+        self.global_idx, self.dtype = tuple(gl), dtype
+        W = (ctypes.c_int32 * heads)(*win)
+        D = (ctypes.c_int32 * heads)(*dil)
+        G = (ctypes.c_int32 * max(1, len(gl)))(*gl) if gl else None
+        p = _Params(batch, heads, n, d, W, D, int(bool(causal)),
+                    ctypes.cast(G, ctypes.POINTER(ctypes.c_int32)) if G else None,
+                    len(gl), _DT[dtype])
+        h = ctypes.c_void_p()
+        _check(self._lib, self._lib.swattn_create(ctypes.byref(p), ctypes.byref(h)),
+               "swattn_create")
+        self._h = h
+
+    def _ptr(self, t, name):
+        if t is None:
+            return None
+        shape = (self.batch, self.heads, self.n, self.d)
+        if not t.is_cuda:
+            raise SwattnError(ERR_INVALID_ARG, f"{name} must be a device tensor")
+        if t.dtype != self.dtype or tuple(t.shape) != shape or not t.is_contiguous():
+            raise SwattnError(ERR_INVALID_ARG,
+                              f"{name} must be contiguous {self.dtype} of shape {shape}")
+        return t.data_ptr()
+
+    def forward(self, q, k, v, qg=None, kg=None, vg=None, out=None, lse=None,
+                want_lse=False, stream=None):
+        """Enqueue one forward on the current stream; returns (out, lse)."""
+        if self._h is None:
+            raise SwattnError(ERR_INVALID_ARG, "plan is closed")
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and want_lse:
+            lse = torch.empty((self.batch, self.heads, self.n), dtype=torch.float32,
+                              device=q.device)
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                                or tuple(lse.shape) != (self.batch, self.heads, self.n)):
+            raise SwattnError(ERR_INVALID_ARG, "lse must be contiguous fp32 [B, H, n]")
+        ptrs = [self._ptr(q, "q"), self._ptr(k, "k"), self._ptr(v, "v"),
+                self._ptr(qg, "qg"), self._ptr(kg, "kg"), self._ptr(vg, "vg"),
+                self._ptr(out, "out"), lse.data_ptr() if lse is not None else None]
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        _check(self._lib, self._lib.swattn_forward(self._h, *ptrs, ctypes.c_void_p(st.cuda_stream)),
+               "swattn_forward")
+        return out, lse
+
+    __call__ = forward
+
+    def set_timing(self, enable=True):
+        """Record HIP events around each kernel phase of later forwards."""
+        _check(self._lib, self._lib.swattn_set_timing(self._h, int(bool(enable))),
+               "swattn_set_timing")
+
+    def kernel_times(self):
+        """(band_ms, global_ms, count): average phase durations since the
+        last call, measured with HIP events on the forward's stream."""
+        b, g, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_int()
+        _check(self._lib, self._lib.swattn_kernel_times(self._h, ctypes.byref(b),
+                                                        ctypes.byref(g), ctypes.byref(c)),
+               "swattn_kernel_times")
+        return b.value, g.value, c.value
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            _check(self._lib, self._lib.swattn_destroy(self._h), "swattn_destroy")
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,293 @@
+// Host side of the C ABI declared in include/swattn.h: validation, plan
+// construction (per-head table, residue-class tile schedule, sorted global
+// index list, global-row workspace) and the stream-ordered launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "swattn.h"
+#include "kernels.hpp"
+
+using namespace swattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SWATTN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Global-row pass: number of key chunks per (row block, b*h). Enough chunks
+// to put a few thousand waves in flight; each chunk a multiple of 64 keys.
+void choose_split(long bh, int nqb, int n, int* nsplit, int* ksplit) {
+  const long target_waves = 2048;
+  long want = (target_waves + bh * nqb - 1) / (bh * nqb);
+  const int max_split = (n + KT - 1) / KT;
+  want = std::max(1L, std::min<long>(want, max_split));
+  int ks = (int)(((n + want - 1) / want + KT - 1) / KT) * KT;
+  *ksplit = ks;
+  *nsplit = (n + ks - 1) / ks;
+}
+
+}  // namespace
+
+struct swattn_plan {
+  int B, H, n, d, causal, ng, dtype, device;
+  int ntiles;
+  int nsplit, ksplit, nqb;
+  void* dev_mem;          // one allocation, carved below
+  HeadInfo* heads;        // [H]
+  int4* tiles;            // [ntiles]
+  int* gidx;              // [ng]
+  float* part_o;          // [B*H][ng][nsplit][64]
+  float* part_ml;         // [B*H][ng][nsplit][2]
+  // measurement hooks
+  static constexpr int kMaxTimed = 4096;
+  std::vector<hipEvent_t> ev;  // [kMaxTimed][4]: band start/stop, global start/stop
+  int ntimed = 0;
+};
+
+extern "C" const char* swattn_status_string(int status) {
+  switch (status) {
+    case SWATTN_OK: return "SWATTN_OK";
+    case SWATTN_ERR_INVALID_ARG: return "SWATTN_ERR_INVALID_ARG";
+    case SWATTN_ERR_UNSUPPORTED: return "SWATTN_ERR_UNSUPPORTED";
+    case SWATTN_ERR_HIP: return "SWATTN_ERR_HIP";
+    case SWATTN_ERR_ALIGNMENT: return "SWATTN_ERR_ALIGNMENT";
+    default: return "SWATTN_UNKNOWN_STATUS";
+  }
+}
+
+extern "C" const char* swattn_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
+  g_last_error.clear();
+  if (!p || !out) return fail(SWATTN_ERR_INVALID_ARG, "params and out must not be NULL");
+  if (p->batch < 1 || p->heads < 1) return fail(SWATTN_ERR_INVALID_ARG, "batch and heads must be >= 1");
+  if (p->n < 1 || p->n > (1 << 24)) return fail(SWATTN_ERR_INVALID_ARG, "n must be in [1, 2^24]");
+  if (p->causal != 0 && p->causal != 1) return fail(SWATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!p->window || !p->dilation) return fail(SWATTN_ERR_INVALID_ARG, "window and dilation must not be NULL");
+  for (int h = 0; h < p->heads; ++h) {
+    if (p->window[h] < 0 || (p->window[h] & 1))
+      return fail(SWATTN_ERR_INVALID_ARG, "window[" + std::to_string(h) + "] must be even and >= 0");
+    if (p->dilation[h] < 1)
+      return fail(SWATTN_ERR_INVALID_ARG, "dilation[" + std::to_string(h) + "] must be >= 1");
+  }
+  if (p->n_global < 0 || p->n_global > p->n) return fail(SWATTN_ERR_INVALID_ARG, "n_global must be in [0, n]");
+  if (p->n_global > 0 && !p->global_idx) return fail(SWATTN_ERR_INVALID_ARG, "global_idx must not be NULL when n_global > 0");
+  std::vector<int> G;
+  if (p->n_global > 0) {
+    G.assign(p->global_idx, p->global_idx + p->n_global);
+    for (int x : G)
+      if (x < 0 || x >= p->n) return fail(SWATTN_ERR_INVALID_ARG, "global index out of [0, n)");
+    std::sort(G.begin(), G.end());
+    if (std::adjacent_find(G.begin(), G.end()) != G.end())
+      return fail(SWATTN_ERR_INVALID_ARG, "global_idx repeats an index");
+  }
+  if (p->d != HD) return fail(SWATTN_ERR_UNSUPPORTED, "only d = 64 is supported");
+  if (p->dtype != SWATTN_BF16 && p->dtype != SWATTN_FP32) return fail(SWATTN_ERR_UNSUPPORTED, "unknown dtype");
+  const long bh = (long)p->batch * p->heads;
+  if (bh * p->n > (1L << 31)) return fail(SWATTN_ERR_UNSUPPORTED, "batch*heads*n must be <= 2^31");
+  // The global-row grid has max(~2048, ceil(|G|/32) * B*H) blocks (see
+  // choose_split) and the merge grid |G| * B*H <= B*H*n: both fit in 2^31.
+
+  // per-head table; a window or dilation beyond n behaves as if clipped to n
+  std::vector<HeadInfo> heads(p->heads);
+  for (int h = 0; h < p->heads; ++h) {
+    const int half = std::min(p->window[h] / 2, p->n);
+    const int dil = std::min(p->dilation[h], p->n);
+    heads[h] = HeadInfo{half, p->causal ? 0 : half, dil, 0};
+  }
+  // tile schedule: (b, h, residue r, 128-row block), neighbours adjacent
+  std::vector<int4> tiles;
+  for (int b = 0; b < p->batch; ++b)
+    for (int h = 0; h < p->heads; ++h) {
+      const int dil = heads[h].dil;
+      for (int r = 0; r < dil; ++r) {
+        const int nr = (p->n - r + dil - 1) / dil;
+        for (int q0 = 0; q0 < nr; q0 += BM) tiles.push_back(make_int4(b * p->heads + h, r, q0, 0));
+      }
+    }
+  if (tiles.size() > (size_t)0x7fffffff) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
+
+  swattn_plan* pl = new (std::nothrow) swattn_plan();
+  if (!pl) return fail(SWATTN_ERR_HIP, "host allocation failed");
+  pl->B = p->batch; pl->H = p->heads; pl->n = p->n; pl->d = p->d;
+  pl->causal = p->causal; pl->ng = p->n_global; pl->dtype = p->dtype;
+  pl->ntiles = (int)tiles.size();
+  pl->nqb = (pl->ng + 31) / 32;
+  pl->nsplit = pl->ksplit = 0;
+  if (pl->ng > 0) choose_split(bh, pl->nqb, p->n, &pl->nsplit, &pl->ksplit);
+  hipError_t e = hipGetDevice(&pl->device);
+  if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
+
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t sz_heads = al(sizeof(HeadInfo) * heads.size());
+  const size_t sz_tiles = al(sizeof(int4) * tiles.size());
+  const size_t sz_g = al(sizeof(int) * std::max<size_t>(G.size(), 1));
+  const size_t nslot = (size_t)bh * pl->ng * pl->nsplit;
+  const size_t sz_po = al(sizeof(float) * HD * nslot);
+  const size_t sz_pml = al(sizeof(float) * 2 * nslot);
+  const size_t total = sz_heads + sz_tiles + sz_g + sz_po + sz_pml;
+  e = hipMalloc(&pl->dev_mem, total);
+  if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
+  char* m = static_cast<char*>(pl->dev_mem);
+  pl->heads = reinterpret_cast<HeadInfo*>(m); m += sz_heads;
+  pl->tiles = reinterpret_cast<int4*>(m); m += sz_tiles;
+  pl->gidx = reinterpret_cast<int*>(m); m += sz_g;
+  pl->part_o = reinterpret_cast<float*>(m); m += sz_po;
+  pl->part_ml = reinterpret_cast<float*>(m);
+  e = hipMemcpy(pl->heads, heads.data(), sizeof(HeadInfo) * heads.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(int4) * tiles.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(pl->dev_mem);
+    delete pl;
+    return hip_fail(e, "hipMemcpy(plan)");
+  }
+  *out = pl;
+  return SWATTN_OK;
+}
+
+namespace {
+void destroy_events(swattn_plan* pl) {
+  for (hipEvent_t x : pl->ev) (void)hipEventDestroy(x);
+  pl->ev.clear();
+  pl->ntimed = 0;
+}
+}  // namespace
+
+extern "C" int swattn_set_timing(swattn_plan* pl, int enable) {
+  g_last_error.clear();
+  if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
+  destroy_events(pl);
+  if (!enable) return SWATTN_OK;
+  pl->ev.resize((size_t)swattn_plan::kMaxTimed * 4, nullptr);
+  for (auto& x : pl->ev) {
+    hipError_t e = hipEventCreate(&x);
+    if (e != hipSuccess) { x = nullptr; destroy_events(pl); return hip_fail(e, "hipEventCreate"); }
+  }
+  return SWATTN_OK;
+}
+
+extern "C" int swattn_kernel_times(swattn_plan* pl, float* band_ms, float* global_ms, int* count) {
+  g_last_error.clear();
+  if (!pl || !band_ms || !global_ms || !count) return fail(SWATTN_ERR_INVALID_ARG, "NULL argument");
+  double sb = 0, sg = 0;
+  const int nt = std::min(pl->ntimed, swattn_plan::kMaxTimed);
+  for (int i = 0; i < nt && !pl->ev.empty(); ++i) {
+    float a = 0, b = 0;
+    hipError_t e = hipEventSynchronize(pl->ev[4 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&a, pl->ev[4 * i + 0], pl->ev[4 * i + 1]);
+    if (e == hipSuccess && pl->ng > 0) {
+      e = hipEventSynchronize(pl->ev[4 * i + 3]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&b, pl->ev[4 * i + 2], pl->ev[4 * i + 3]);
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    sb += a; sg += b;
+  }
+  *count = nt;
+  *band_ms = nt ? (float)(sb / nt) : 0.f;
+  *global_ms = nt ? (float)(sg / nt) : 0.f;
+  pl->ntimed = 0;
+  return SWATTN_OK;
+}
+
+extern "C" int swattn_destroy(swattn_plan* plan) {
+  g_last_error.clear();
+  if (!plan) return SWATTN_OK;
+  destroy_events(plan);
+  hipError_t e = hipFree(plan->dev_mem);
+  delete plan;
+  if (e != hipSuccess) return hip_fail(e, "hipFree(plan)");
+  return SWATTN_OK;
+}
+
+namespace {
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+template <class T>
+int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const void* qg,
+           const void* kg, const void* vg, void* o, float* lse, hipStream_t st) {
+  const float scale = 0.125f;  // 1/sqrt(64)
+  BandParams bp;
+  bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.lse = lse;
+  bp.tiles = pl->tiles; bp.heads = pl->heads; bp.gidx = pl->gidx; bp.ng = pl->ng;
+  bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
+  bp.c2 = scale * LOG2E; bp.scale = scale;
+  const bool timed = !pl->ev.empty() && pl->ntimed < swattn_plan::kMaxTimed;
+  hipEvent_t* ev = timed ? &pl->ev[4 * (size_t)pl->ntimed] : nullptr;
+  if (timed) pl->ntimed++;
+  hipError_t e = hipSuccess;
+  if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  hipLaunchKernelGGL(band_fwd<T>, dim3(pl->ntiles), dim3(256), 0, st, bp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch band_fwd");
+  if (timed && (e = hipEventRecord(ev[1], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (pl->ng > 0) {
+    if (timed && (e = hipEventRecord(ev[2], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    GlobalParams gp;
+    gp.qg = qg; gp.kg = kg; gp.vg = vg; gp.o = o; gp.lse = lse; gp.gidx = pl->gidx;
+    gp.part_o = pl->part_o; gp.part_ml = pl->part_ml;
+    gp.ng = pl->ng; gp.n = pl->n; gp.causal = pl->causal;
+    gp.nsplit = pl->nsplit; gp.ksplit = pl->ksplit; gp.nqb = pl->nqb;
+    gp.c2 = scale * LOG2E; gp.scale = scale;
+    const int bh = pl->B * pl->H;
+    hipLaunchKernelGGL(global_rows_partial<T>, dim3(pl->nsplit * pl->nqb * bh), dim3(64), 0, st, gp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch global_rows_partial");
+    hipLaunchKernelGGL(global_rows_merge<T>, dim3(pl->ng * bh), dim3(64), 0, st, gp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch global_rows_merge");
+    if (timed && (e = hipEventRecord(ev[3], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return SWATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int swattn_forward(swattn_plan* pl, const void* q, const void* k, const void* v,
+                              const void* qg, const void* kg, const void* vg, void* o,
+                              float* lse, void* stream) {
+  g_last_error.clear();
+  if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
+  if (!q || !k || !v || !o) return fail(SWATTN_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+  const bool want_g = pl->ng > 0;
+  if ((qg != nullptr) != want_g || (kg != nullptr) != want_g || (vg != nullptr) != want_g)
+    return fail(SWATTN_ERR_INVALID_ARG, "qg, kg, vg must be non-NULL exactly when n_global > 0");
+  const void* all[] = {q, k, v, qg, kg, vg, o, lse};
+  for (const void* x : all)
+    if (x && !aligned16(x)) return fail(SWATTN_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const size_t es = pl->dtype == SWATTN_BF16 ? 2 : 4;
+  const size_t nbytes = (size_t)pl->B * pl->H * pl->n * HD * es;
+  const void* ins[] = {q, k, v, qg, kg, vg};
+  for (const void* x : ins)
+    if (overlaps(o, nbytes, x, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse) {
+    const size_t lb = (size_t)pl->B * pl->H * pl->n * sizeof(float);
+    for (const void* x : ins)
+      if (overlaps(lse, lb, x, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "lse overlaps an input");
+    if (overlaps(lse, lb, o, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "lse overlaps o");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pl->dtype == SWATTN_BF16) return launch<__bf16>(pl, q, k, v, qg, kg, vg, o, lse, st);
+  return launch<float>(pl, q, k, v, qg, kg, vg, o, lse, st);
+}

@@ -32,7 +32,8 @@ def test_sharp_and_dedup_kinds():
     s = make_inputs(wl, 0, "sharp")
     assert s["v"].float().abs().max() <= 1.0 and s["q"].float().std() > 1.5
     d = make_inputs(wl, 0, "dedup")
-    assert (d["v"][0, 0, :64].float().sum(-1) == 8.0).all()
+    assert (d["v"][0, 0, [0, 16, 32, 48]].float().sum(-1) == 1.0).all()
+    assert torch.equal(d["k"][0, 0, 0], d["k"][0, 0, 16])
 
 
 def test_accounting_matches_hand_counts():
