@@ -7,17 +7,18 @@
 // global tokens attend to every key through the separate projections Qg, Kg,
 // Vg. Softmax scale 1/sqrt(64).
 //
-// Work decomposition (all three kernels share the wave-level tile engine):
+// Work decomposition (all kernels share the wave-level 32-key unit below):
 //  * band_fwd: one workgroup = 4 waves = 128 query rows of one residue class
 //    r (rows r, r+dil, r+2*dil, ... of one (batch, head)); within a residue
 //    class the dilated window is an ordinary window of w+1 keys, so K/V rows
 //    are read with a row stride of dil*64 elements and no key is wasted on
-//    the gaps. Key tiles of 64 rows are double-buffered in LDS and shared by
-//    the 4 waves; each wave skips the 32-key halves that lie outside its own
-//    32 rows' band. The global columns are extra key tiles gathered from
-//    K[G], V[G], masked so that a global key already inside the band is not
-//    counted twice; the running max/sum of the online softmax merges them
-//    with the band exactly as a log-sum-exp merge would.
+//    the gaps. Key tiles of 64 rows stream through a 3-stage LDS ring filled
+//    by direct global->LDS loads, shared by the 4 waves; each wave skips the
+//    32-key units that lie outside its own 32 rows' band. The global columns
+//    are extra key tiles gathered from K[G], V[G], masked so that a global key
+//    already inside the band is not counted twice; the running max/sum of
+//    the online softmax merges them with the band exactly as a log-sum-exp
+//    merge would.
 //  * global_rows_partial: rows of G against a chunk of all keys with Qg, Kg,
 //    Vg; writes an unnormalised partial (o, m, l) per chunk.
 //  * global_rows_merge: log-sum-exp merge of the chunks; overwrites rows G of
@@ -42,8 +43,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 #define DEV __device__ __forceinline__
 
@@ -118,14 +122,14 @@ DEV int swz(int row) {
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
 }
 
-// MFMA row r of the S^T tile -> key within the 32-key half (swap bits 2, 3).
+// MFMA row r of the S^T tile -> key within the 32-key unit (swap bits 2, 3).
 DEV int kperm16(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 // fp32 variant: MFMA row r = 8a + 4g + b -> key 8a + 2b + g.
 DEV int kperm32(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// key (within the 32-key half) held by accumulator register j of lane group g
-DEV int key_of_reg16(int j, int g) { return ((j >> 3) << 4) + (g << 3) + (j & 7); }
-DEV int key_of_reg32(int j, int g) { return 2 * j + g; }
+// key (within the 32-key unit) held by accumulator register j of lane group g
+DEV constexpr int key_of_reg16(int j, int g) { return ((j >> 3) << 4) + (g << 3) + (j & 7); }
+DEV constexpr int key_of_reg32(int j, int g) { return 2 * j + g; }
 
 DEV f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -134,26 +138,53 @@ DEV f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-DEV float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Values of lane l and lane l^32, returned as (lo-half copy, hi-half copy):
+// max/sum of the two is the pair's max/sum on every lane.
+DEV f32x2 pair_swap(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f32x2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+DEV float pair_max(float x) { const f32x2 t = pair_swap(x); return fmaxf(t[0], t[1]); }
+DEV float pair_sum(float x) { const f32x2 t = pair_swap(x); return t[0] + t[1]; }
+
+// A workgroup barrier that does not wait for outstanding global->LDS loads
+// (the loads of the next tiles stay in flight); the asm statements keep the
+// compiler from moving memory accesses across it.
+DEV void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N> DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
 
 template <class T> struct ElemTraits;
 template <> struct ElemTraits<__bf16> {
   static constexpr int ROWB = 128;           // bytes per K/V row
   static constexpr int CPR = ROWB / 16;      // 16-byte chunks per row
-  static DEV int lds_off(int row, int ch) { return row * ROWB + ((ch ^ swz(row)) << 4); }
+  static DEV int phys(int row, int ch) { return ch ^ swz(row); }  // involution
+  static DEV int lds_off(int row, int ch) { return row * ROWB + (phys(row, ch) << 4); }
 };
 template <> struct ElemTraits<float> {
   static constexpr int ROWB = 256;
   static constexpr int CPR = ROWB / 16;
+  static DEV int phys(int, int ch) { return ch; }
   static DEV int lds_off(int row, int ch) { return row * ROWB + (ch << 4); }
 };
 
 // ----------------------------------------------------------------------------
-// Wave-level tile engine.
+// Wave-level engine.
 //
-// State of one wave: 32 query rows (one per lane pair l, l+32), running max m
-// (raw score units), this lane's partial sum l, and O^T accumulators for the
-// two 32-wide halves of d.
+// State of one wave: 32 query rows (lane l and lane l^32 share row l%32),
+// reference max m (raw score units; the same on both lanes of a row), this
+// lane's partial row sum l, and O^T accumulators for the two 32-wide halves
+// of d.
 template <class T> struct QFrag;
 template <> struct QFrag<__bf16> { bf16x8 v[4]; };  // d = 16s + 8g + e
 template <> struct QFrag<float> { float v[32]; };   // d = 2s + g
@@ -165,6 +196,7 @@ struct WaveAcc {
 };
 
 DEV void acc_init(WaveAcc& a) {
+#pragma unroll
   for (int i = 0; i < 16; ++i) { a.o[0][i] = 0.f; a.o[1][i] = 0.f; }
   a.m = -__builtin_inff();
   a.l = 0.f;
@@ -173,102 +205,250 @@ DEV void acc_init(WaveAcc& a) {
 // Load the B operand of S^T = K Q^T for this lane's query row (global memory).
 DEV void load_q(QFrag<__bf16>& qf, const __bf16* row, int g) {
   const uint4* p = reinterpret_cast<const uint4*>(row);
+#pragma unroll
   for (int s = 0; s < 4; ++s) qf.v[s] = __builtin_bit_cast(bf16x8, p[2 * s + g]);
 }
 DEV void load_q(QFrag<float>& qf, const float* row, int g) {
+#pragma unroll
   for (int s = 0; s < 32; ++s) qf.v[s] = row[2 * s + g];
 }
 
-// S^T for one 32-key half of the LDS tile: 16 fp32 values per lane.
-DEV f32x16 score_half(const char* kbuf, int kh, const QFrag<__bf16>& qf, int lane) {
+// S^T for one 32-key unit (rows 32*kh .. 32*kh+31 of the LDS tile).
+DEV f32x16 score_unit(const char* kbuf, int kh, const QFrag<__bf16>& qf, int lane) {
   const int g = lane >> 5;
   const int row = kperm16(lane & 31) + 32 * kh;
-  f32x16 s;
-  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+  f32x16 s = {};
+#pragma unroll
   for (int st = 0; st < 4; ++st) {
     bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + ElemTraits<__bf16>::lds_off(row, 2 * st + g));
     s = mfma_bf16(a, qf.v[st], s);
   }
   return s;
 }
-DEV f32x16 score_half(const char* kbuf, int kh, const QFrag<float>& qf, int lane) {
+DEV f32x16 score_unit(const char* kbuf, int kh, const QFrag<float>& qf, int lane) {
   const int g = lane >> 5;
   const int row = kperm32(lane & 31) + 32 * kh;
   const float* kr = reinterpret_cast<const float*>(kbuf + row * ElemTraits<float>::ROWB);
-  f32x16 s;
-  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+  f32x16 s = {};
+#pragma unroll
   for (int st = 0; st < 32; ++st) s = mfma_f32(kr[2 * st + g], qf.v[st], s);
   return s;
 }
 
-// O^T += V^T P^T for one 32-key half whose probabilities are p (accumulator
-// layout of score_half).
-DEV void pv_half(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane) {
+// O^T += V^T P^T for one 32-key unit whose probabilities are p (accumulator
+// layout of score_unit).
+DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane, __bf16) {
   const int g = lane >> 5;
   const int i16 = lane & 15;
+#pragma unroll
   for (int sp = 0; sp < 2; ++sp) {
     bf16x8 b;
-    for (int e = 0; e < 8; ++e) b[e] = (__bf16)p[8 * sp + e];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 t = __builtin_convertvector(f32x2{p[8 * sp + e], p[8 * sp + e + 1]}, bf16x2);
+      b[e] = t[0];
+      b[e + 1] = t[1];
+    }
+#pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
+      // Source lane i16 of each 16-lane group points at 4 d-contiguous
+      // elements of key key0 + i16/4, columns d0 + 4*(i16%4) ..+3; the
+      // transposed read hands lane i16 the 4 keys at column d0 + i16.
       const int d0 = 32 * dh + 16 * ((lane >> 4) & 1);
-      bf16x8 a;
-      for (int hx = 0; hx < 2; ++hx) {
-        // source lane (as a 16-lane group member) points at 4 d-contiguous
-        // elements of key key0 + i16/4, columns d0 + 4*(i16%4) ..+3; the
-        // transposed read hands lane i16 the 4 keys at column d0 + i16.
-        const int key0 = 32 * kh + 16 * sp + 8 * g + 4 * hx;
-        const int row = key0 + (i16 >> 2);
-        const int col = d0 + 4 * (i16 & 3);
-        const char* src = vbuf + ElemTraits<__bf16>::lds_off(row, col >> 3) + ((col & 7) << 1);
-        s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
-        bf16x4 tb = __builtin_bit_cast(bf16x4, t);
-        for (int e = 0; e < 4; ++e) a[4 * hx + e] = tb[e];
-      }
-      acc.o[dh] = mfma_bf16(a, b, acc.o[dh]);
+      const int col = d0 + 4 * (i16 & 3);
+      const int key0 = 32 * kh + 16 * sp + 8 * g;
+      const int row0 = key0 + (i16 >> 2), row1 = row0 + 4;
+      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vbuf + ElemTraits<__bf16>::lds_off(row0, col >> 3) + ((col & 7) << 1)));
+      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(vbuf + ElemTraits<__bf16>::lds_off(row1, col >> 3) + ((col & 7) << 1)));
+      const s16x8 a = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc.o[dh] = mfma_bf16(__builtin_bit_cast(bf16x8, a), b, acc.o[dh]);
     }
   }
 }
-DEV void pv_half_f32(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane) {
+DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane, float) {
   const int g = lane >> 5;
+#pragma unroll
   for (int t = 0; t < 16; ++t) {
     const float* vr = reinterpret_cast<const float*>(vbuf + (32 * kh + 2 * t + g) * ElemTraits<float>::ROWB);
+#pragma unroll
     for (int dh = 0; dh < 2; ++dh) acc.o[dh] = mfma_f32(vr[32 * dh + (lane & 31)], p[t], acc.o[dh]);
   }
 }
 
-// Online-softmax update of one 64-key tile. s[kh] holds raw scores with
-// masked entries at -inf; active[kh] says whether half kh was computed.
-// Afterwards s[kh] holds the probabilities (relative to the new max).
+template <class T> DEV constexpr int key_of_reg(int j, int g) {
+  if constexpr (sizeof(T) == 2) return key_of_reg16(j, g);
+  else return key_of_reg32(j, g);
+}
+
+// Online-softmax update and P V for one 32-key unit whose raw scores are s
+// (masked entries at -inf).
+//
+// The reference max m is raised only when a row's unit max exceeds it by more
+// than RESCALE_LOG2 in the exp2 domain (then O and l are rescaled, and both
+// lanes of the row agree on the new m); otherwise probabilities relative to
+// the stale m stay below 2^RESCALE_LOG2, which fp32 accumulators and the bf16
+// P operand hold without loss of relative precision. O = acc / l and
+// LSE = m*scale + ln l are the same quantities as with an exact running max.
+constexpr float RESCALE_LOG2 = 8.0f;
+
 template <class T>
-DEV void softmax_tile(WaveAcc& acc, f32x16 (&s)[2], const bool (&active)[2], float c2) {
-  float mx = -__builtin_inff();
-  for (int kh = 0; kh < 2; ++kh)
-    if (active[kh])
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kh][j]);
-  mx = fmaxf(mx, wave_xor32(mx));
-  const float mnew = fmaxf(acc.m, mx);
-  const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f((acc.m - muse) * c2);
-  const float moff = -muse * c2;
-  float lsum = 0.f;
-  for (int kh = 0; kh < 2; ++kh) {
-    if (!active[kh]) continue;
-    for (int j = 0; j < 16; ++j) {
-      const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kh][j], c2, moff));
-      s[kh][j] = pj;
-      lsum += pj;
-    }
-  }
-  acc.l = acc.l * alpha + lsum;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+DEV void softmax_pv_unit(WaveAcc& acc, f32x16 s, const char* vbuf, int kh, int lane, float c2) {
+  float mx = s[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+  const float thr = acc.m * c2 + RESCALE_LOG2;
+  if (__builtin_amdgcn_ballot_w64(mx * c2 > thr)) {
+    const float pm = pair_max(mx);
+    const bool upd = pm * c2 > thr;  // the same decision on both lanes of a row
+    // rows that do not move keep alpha = 1 (also while their m is still -inf)
+    const float alpha = upd ? __builtin_amdgcn_exp2f((acc.m - pm) * c2) : 1.0f;
+#pragma unroll
     for (int i = 0; i < 16; ++i) { acc.o[0][i] *= alpha; acc.o[1][i] *= alpha; }
+    acc.l *= alpha;
+    acc.m = upd ? pm : acc.m;
   }
-  acc.m = mnew;
+  // a row with every key masked so far has m = -inf and only -inf scores
+  const float moff = acc.m == -__builtin_inff() ? 0.f : -acc.m * c2;
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, moff));
+    s[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, moff));
+    l0 += s[j];
+    l1 += s[j + 1];
+  }
+  acc.l += l0 + l1;
+  pv_unit(acc, vbuf, kh, s, lane, T{});
+}
+
+// Mask one 32-key unit of a band tile: key kk = k0 + key_of_reg(j, g) is
+// allowed for query qi iff qi - half <= kk <= min(qi + right, nr - 1).
+template <class T>
+DEV void mask_band_unit(f32x16& s, int k0, int qi, int half, int right, int nr, int g) {
+  const int lo = qi - half - k0;
+  const int hi = min(qi + right, nr - 1) - k0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int off = key_of_reg<T>(j, g);
+    if (off < lo || off > hi) s[j] = -__builtin_inff();
+  }
+}
+
+// Store the normalised O rows owned by this lane (query row `pos`).
+DEV void store_o(__bf16* orow, const WaveAcc& acc, float inv, int g) {
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(acc.o[dh][4 * a + e] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 32 * dh + 8 * a + 4 * g) = t;
+    }
+}
+DEV void store_o(float* orow, const WaveAcc& acc, float inv, int g) {
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = acc.o[dh][4 * a + e] * inv;
+      *reinterpret_cast<f32x4*>(orow + 32 * dh + 8 * a + 4 * g) = t;
+    }
 }
 
 // ----------------------------------------------------------------------------
-// Cooperative tile loads: NT threads move 64 rows of K and V into LDS.
+// Tile movement.
 
+// Direct global->LDS load of one 64-row K tile and V tile (rows
+// r + kk*dil, kk = kb0 .. kb0+63 clamped to kend-1) into `stage` (K at 0, V
+// at KT*ROWB). Each wave issues PER_WAVE 1-KB instructions; lane l of an
+// instruction lands at LDS byte 16*l of it, so it fetches the logical chunk
+// that the swizzle places there.
+template <class T>
+struct Dma {
+  static constexpr int ROWB = ElemTraits<T>::ROWB;
+  static constexpr int CPR = ElemTraits<T>::CPR;
+  static constexpr int RPI = 1024 / ROWB;            // rows per instruction
+  static constexpr int NI = 2 * KT * ROWB / 1024;     // instructions per K+V tile
+  static constexpr int PER_WAVE = NI / BAND_WAVES;    // per wave (bf16: 4, fp32: 8)
+};
+
+// One 16-byte-per-lane global->LDS load; `lds` is the wave-uniform LDS byte
+// address of the 1-KB destination (held in M0). Written as a statement of its
+// own so that the compiler does not track it as an LDS store: the band loop
+// orders these loads against LDS reads itself (wait_vmcnt + wg_barrier). The
+// instruction has no register result, so nothing is overwritten in flight.
+DEV void dma16(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+template <class T>
+DEV void dma_tile(unsigned stage, const char* kb, const char* vb, int kb0, int kend, int r, int dil,
+                  int wave, int lane) {
+  using D = Dma<T>;
+#pragma unroll
+  for (int i = 0; i < D::PER_WAVE; ++i) {
+    const int I = wave * D::PER_WAVE + i;  // wave-uniform
+    const int tensor = I / (D::NI / 2);
+    const int blk = I % (D::NI / 2);
+    const int row = blk * D::RPI + lane / D::CPR;
+    const int pc = lane % D::CPR;
+    const int kk = min(kb0 + row, kend - 1);
+    const char* src = (tensor ? vb : kb) + (long)(r + kk * dil) * D::ROWB +
+                      (ElemTraits<T>::phys(row, pc) << 4);
+    dma16(src, stage + (unsigned)(tensor * (KT * D::ROWB) + blk * 1024));
+  }
+}
+
+// The same loads for a tile whose 64 rows all exist (kb0 + 63 < kend), with
+// a wave-uniform 64-bit base in SGPRs and a loop-invariant 32-bit lane
+// offset: address = kb|vb + (r + kb0*dil)*ROWB + blk*RPI*dil*ROWB + lane_off.
+// The lane offset (row-within-block * dil * ROWB + swizzled chunk) depends
+// only on the parity of the block (the swizzle reads bit 3 of the row), so
+// two registers cover every instruction.
+DEV void dma16_saddr(const char* base, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+template <class T>
+struct DmaLanes {
+  unsigned off[2];  // lane offset for even / odd blocks
+};
+
+template <class T>
+DEV void dma_lanes_init(DmaLanes<T>& dl, int dil, int lane) {
+  using D = Dma<T>;
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int row = par * D::RPI + lane / D::CPR;  // row within an even/odd block pair
+    const int pc = lane % D::CPR;
+    dl.off[par] = (unsigned)((lane / D::CPR) * dil * D::ROWB + (ElemTraits<T>::phys(row, pc) << 4));
+  }
+}
+
+template <class T>
+DEV void dma_tile_fast(unsigned stage, const DmaLanes<T>& dl, const char* kb, const char* vb,
+                       int kb0, int r, int dil, int wave) {
+  using D = Dma<T>;
+  const long rowb = (long)(r + kb0 * dil) * D::ROWB;  // wave-uniform
+#pragma unroll
+  for (int i = 0; i < D::PER_WAVE; ++i) {
+    const int I = wave * D::PER_WAVE + i;
+    const int tensor = I / (D::NI / 2);
+    const int blk = I % (D::NI / 2);
+    const char* base = (tensor ? vb : kb) + rowb + (long)blk * D::RPI * dil * D::ROWB;
+    dma16_saddr(base, dl.off[blk & 1], stage + (unsigned)(tensor * (KT * D::ROWB) + blk * 1024));
+  }
+}
+
+// Register-staged tile movement (used by the global-column prologue and the
+// global-row kernel).
 template <class T, int NT>
 struct TileRegs {
   static constexpr int NC = KT * ElemTraits<T>::CPR / NT;  // chunks per thread per tensor
@@ -276,42 +456,10 @@ struct TileRegs {
   uint4 v[NC];
 };
 
-// Row of tile-local key `row`: returns the sequence position or -1 (padding).
-struct BandRowMap {
-  int kbase, kend, r, dil;
-  DEV int pos(int row) const { int kk = kbase + row; return kk < kend ? r + kk * dil : -1; }
-};
-struct GlobalRowMap {
-  const int* gidx;
-  int base, ng;
-  DEV int pos(int row) const { int i = base + row; return i < ng ? gidx[i] : -1; }
-};
-struct PlainRowMap {
-  int kbase, kend;
-  DEV int pos(int row) const { int kk = kbase + row; return kk < kend ? kk : -1; }
-};
-
-template <class T, int NT, class Map>
-DEV void tile_fetch(TileRegs<T, NT>& tr, const char* kb, const char* vb, const Map& map, int tid) {
-  constexpr int CPR = ElemTraits<T>::CPR;
-  for (int u = 0; u < TileRegs<T, NT>::NC; ++u) {
-    const int c = tid + NT * u;
-    const int row = c / CPR, ch = c % CPR;
-    const int pos = map.pos(row);
-    if (pos >= 0) {
-      const long off = (long)pos * ElemTraits<T>::ROWB + ch * 16;
-      tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
-      tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
-    } else {
-      tr.k[u] = make_uint4(0, 0, 0, 0);
-      tr.v[u] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
 template <class T, int NT>
 DEV void tile_commit(const TileRegs<T, NT>& tr, char* klds, char* vlds, int tid) {
   constexpr int CPR = ElemTraits<T>::CPR;
+#pragma unroll
   for (int u = 0; u < TileRegs<T, NT>::NC; ++u) {
     const int c = tid + NT * u;
     const int row = c / CPR, ch = c % CPR;
@@ -321,47 +469,91 @@ DEV void tile_commit(const TileRegs<T, NT>& tr, char* klds, char* vlds, int tid)
   }
 }
 
-template <class T>
-DEV void pv_dispatch(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane) {
-  if constexpr (sizeof(T) == 2) pv_half(acc, vbuf, kh, p, lane);
-  else pv_half_f32(acc, vbuf, kh, p, lane);
-}
-
-template <class T> DEV int key_of_reg(int j, int g) {
-  if constexpr (sizeof(T) == 2) return key_of_reg16(j, g);
-  else return key_of_reg32(j, g);
-}
-
-// Store the normalised O rows owned by this lane (query row `pos`).
-DEV void store_o(__bf16* orow, const WaveAcc& acc, float inv, int g) {
-  for (int dh = 0; dh < 2; ++dh)
-    for (int a = 0; a < 4; ++a) {
-      bf16x4 t;
-      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(acc.o[dh][4 * a + e] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * dh + 8 * a + 4 * g) = t;
-    }
-}
-DEV void store_o(float* orow, const WaveAcc& acc, float inv, int g) {
-  for (int dh = 0; dh < 2; ++dh)
-    for (int a = 0; a < 4; ++a) {
-      f32x4 t;
-      for (int e = 0; e < 4; ++e) t[e] = acc.o[dh][4 * a + e] * inv;
-      *reinterpret_cast<f32x4*>(orow + 32 * dh + 8 * a + 4 * g) = t;
-    }
+// Fetch 64 rows kk = kb0 .. kb0+63 (clamped to kend-1) of K and V.
+template <class T, int NT>
+DEV void plain_fetch(TileRegs<T, NT>& tr, const char* kb, const char* vb, int kb0, int kend, int tid) {
+  constexpr int CPR = ElemTraits<T>::CPR;
+#pragma unroll
+  for (int u = 0; u < TileRegs<T, NT>::NC; ++u) {
+    const int c = tid + NT * u;
+    const int kk = min(kb0 + c / CPR, kend - 1);
+    const long off = (long)kk * ElemTraits<T>::ROWB + (c % CPR) * 16;
+    tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
+    tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
+  }
 }
 
 // ----------------------------------------------------------------------------
 // Band kernel (with the global columns folded in as extra key tiles).
 
+// Per-wave constants of the band loop.
+struct BandWave {
+  unsigned a0, a1, a2;  // LDS byte addresses of the stages (a2 unused with 2)
+  const char* kb;  // K rows of this (batch, head)
+  const char* vb;  // V rows of this (batch, head)
+  int kbeg, kend, nband;  // key tiles: rows kbeg + 64t, clamped to kend - 1
+  int r, dil;
+  int qi, qw0, half, right, nr, wk_lo, wk_hi;
+  int wave, lane, g;
+  bool live;
+  float c2;
+};
+
+// One step of the NS-stage ring (NS = 2 or 3) for tile tb, which sits in
+// stage S: wait for it, publish it to the workgroup, start the DMA of tile
+// tb+NS-1 into stage (S+NS-1)%NS (the stage of tile tb-1, which every wave
+// has finished), and compute it. The stages are distinct LDS objects indexed
+// statically, so the compiler can tell that the reads of stage S do not
+// depend on the loads in flight to the others. Every step issues exactly one
+// tile of DMA (past the last tile it re-fetches the last tile into a stage
+// nobody reads again), so every step's wait has the same count.
+template <class T, int NS, int S>
+DEV void band_step(int tb, WaveAcc& acc, const QFrag<T>& qf, const BandWave& w,
+                   const DmaLanes<T>& dl, const char* st0, const char* st1, const char* st2) {
+  constexpr int TILEB = KT * ElemTraits<T>::ROWB;
+  const char* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
+  constexpr int SN = (S + NS - 1) % NS;
+  const unsigned nxt = SN == 0 ? w.a0 : (SN == 1 ? w.a1 : w.a2);
+  wait_vmcnt<NS == 3 ? Dma<T>::PER_WAVE : 0>();
+  wg_barrier();  // tile tb has landed for every wave; tile tb-1 is consumed
+  const int kn = w.kbeg + min(tb + NS - 1, w.nband - 1) * KT;
+  if (kn + KT <= w.kend) dma_tile_fast<T>(nxt, dl, w.kb, w.vb, kn, w.r, w.dil, w.wave);
+  else dma_tile<T>(nxt, w.kb, w.vb, kn, w.kend, w.r, w.dil, w.wave, w.lane);
+  if (!w.live) return;
+  const int k0 = w.kbeg + tb * KT;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int ku = k0 + 32 * kh;
+    if (ku > w.wk_hi || ku + 31 < w.wk_lo) continue;  // wave-uniform skip
+    f32x16 sc = score_unit(cur, kh, qf, w.lane);
+    const bool interior = ku >= w.qw0 + 31 - w.half && ku + 31 <= w.qw0 + w.right && ku + 31 < w.nr;
+    if (!interior) mask_band_unit<T>(sc, ku, w.qi, w.half, w.right, w.nr, w.g);
+    softmax_pv_unit<T>(acc, sc, cur + TILEB, kh, w.lane, w.c2);
+  }
+}
+
+// LDS ring depth of the band kernel and the resulting waves per SIMD: bf16
+// tiles are 16 KB (K + V), so three stages (48 KB) leave room for three
+// workgroups per CU; fp32 tiles are 32 KB.
+template <class T> struct BandCfg;
+template <> struct BandCfg<__bf16> { static constexpr int NS = 3; };
+template <> struct BandCfg<float> { static constexpr int NS = 2; };
+
 template <class T>
 __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
   constexpr int ROWB = ElemTraits<T>::ROWB;
+  constexpr int CPR = ElemTraits<T>::CPR;
   constexpr int TILEB = KT * ROWB;
-  __shared__ __attribute__((aligned(16))) char lds[2][2][TILEB];
-  __shared__ int gmeta[2][2][KT];  // global tiles: key position, residue-local index
+  constexpr int STAGEB = 2 * TILEB;
+  __shared__ __attribute__((aligned(1024))) char st0[STAGEB];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGEB];
+  constexpr int NS = BandCfg<T>::NS;
+  __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGEB : 1024];
+  __shared__ int gmeta[2][KT];  // global tile: key position, residue-local index
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int4 td = p.tiles[bid];
   const int bh = td.x, r = td.y, q0 = td.z;
@@ -374,9 +566,7 @@ __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
 
   const int kbeg = max(0, q0 - half);
   const int kend = min(nr, q0 + BM + right);
-  const int nband = (kend - kbeg + KT - 1) / KT;
-  const int nglob = (p.ng + KT - 1) / KT;
-  const int ntiles = nglob + nband;
+  const int nband = (kend - kbeg + KT - 1) / KT;  // >= 1: row q0 sees itself
 
   // this wave's query rows and key range (residue-local)
   const int qw0 = q0 + 32 * wave;
@@ -386,86 +576,96 @@ __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
   const int pos_q = r + min(qi, nr - 1) * dil;
   const int wk_lo = max(0, qw0 - half);
   const int wk_hi = min(nr - 1, qw0 + 31 + right);
-  const int lim = p.causal ? pos_q : 0x7fffffff - 1;
 
+  const unsigned a0 = (unsigned)(uintptr_t)(lds_void*)st0;
+  const unsigned a1 = (unsigned)(uintptr_t)(lds_void*)st1;
+  const unsigned a2 = (unsigned)(uintptr_t)(lds_void*)st2;
+  const T* qrow = reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.q) + base + (long)pos_q * ROWB);
   QFrag<T> qf;
-  load_q(qf, reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.q) + base + (long)pos_q * ROWB), g);
   WaveAcc acc;
   acc_init(acc);
-
-  TileRegs<T, 256> tr;
-  auto fetch = [&](int t) {
-    if (t < nglob) {
-      GlobalRowMap m{p.gidx, t * KT, p.ng};
-      tile_fetch<T, 256>(tr, kb, vb, m, tid);
-    } else {
-      BandRowMap m{kbeg + (t - nglob) * KT, kend, r, dil};
-      tile_fetch<T, 256>(tr, kb, vb, m, tid);
-    }
-  };
-  auto commit = [&](int t, int buf) {
-    tile_commit<T, 256>(tr, lds[buf][0], lds[buf][1], tid);
-    if (t < nglob && tid < KT) {
-      const int idx = t * KT + tid;
-      int kp = 0x7fffffff, kr = NEG_SENTINEL;
-      if (idx < p.ng) {
-        kp = p.gidx[idx];
-        const int dr = kp - r;
-        if (dr >= 0 && dr % dil == 0) kr = dr / dil;
-      }
-      gmeta[buf][0][tid] = kp;
-      gmeta[buf][1][tid] = kr;
-    }
-  };
-
-  fetch(0);
-  commit(0, 0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
-    if (wave_live) {
-      const char* kl = lds[buf][0];
-      const char* vl = lds[buf][1];
-      f32x16 s[2];
-      bool active[2];
-      const bool is_glob = t < nglob;
-      const int tkey0 = is_glob ? t * KT : kbeg + (t - nglob) * KT;
-      for (int kh = 0; kh < 2; ++kh) {
-        const int k0 = tkey0 + 32 * kh;
-        active[kh] = is_glob ? (k0 < p.ng) : (k0 <= wk_hi && k0 + 31 >= wk_lo);
-        if (!active[kh]) continue;
-        s[kh] = score_half(kl, kh, qf, lane);
-        if (is_glob) {
-          for (int j = 0; j < 16; ++j) {
-            const int kk = 32 * kh + key_of_reg<T>(j, g);
-            const int kp = gmeta[buf][0][kk], kr = gmeta[buf][1][kk];
-            const bool inband = kr >= qi - half && kr <= qi + right;
-            if (!(kp <= lim) || inband) s[kh][j] = -__builtin_inff();
-          }
-        } else {
-          const bool interior = k0 >= qw0 + 31 - half && k0 + 31 <= qw0 + right && k0 + 31 < nr;
-          if (!interior) {
-            for (int j = 0; j < 16; ++j) {
-              const int kk = k0 + key_of_reg<T>(j, g);
-              if (kk < qi - half || kk > qi + right || kk >= nr) s[kh][j] = -__builtin_inff();
-            }
-          }
-        }
-      }
-      if (active[0] || active[1]) {
-        softmax_tile<T>(acc, s, active, p.c2);
-        for (int kh = 0; kh < 2; ++kh)
-          if (active[kh]) pv_dispatch<T>(acc, vl, kh, s[kh], lane);
-      }
-    }
-    if (t + 1 < ntiles) commit(t + 1, buf ^ 1);
-    __syncthreads();
+  if (p.ng == 0) {
+    // start the first two band tiles, then Q; one wait covers all of them
+    // (the compiler must not see Q in flight inside the band loop, where it
+    // does not know about the tile loads)
+    dma_tile<T>(a0, kb, vb, kbeg, kend, r, dil, wave, lane);
+    if (NS == 3) dma_tile<T>(a1, kb, vb, kbeg + min(1, nband - 1) * KT, kend, r, dil, wave, lane);
+    load_q(qf, qrow, g);
+    wait_vmcnt<0>();
+  } else {
+    load_q(qf, qrow, g);
+    wait_vmcnt<0>();
   }
 
+  // (1) global columns: tiles of up to 64 keys gathered from K[G], V[G] into
+  // stage 0. A key is used by a row only if it is left of the row (when
+  // causal) and not already inside the row's band.
+  if (p.ng > 0) {
+    constexpr int NC = TileRegs<T, 256>::NC;
+    const int lim = p.causal ? pos_q : 0x7fffffff - 1;
+    for (int t0 = 0; t0 < p.ng; t0 += KT) {
+      TileRegs<T, 256> tr;
+      int gp[NC];
+#pragma unroll
+      for (int u = 0; u < NC; ++u) gp[u] = p.gidx[min(t0 + (tid + 256 * u) / CPR, p.ng - 1)];
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const long off = (long)gp[u] * ROWB + ((tid + 256 * u) % CPR) * 16;
+        tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
+        tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
+      }
+      if (tid < KT) {
+        int kp = 0x7fffffff, kr = NEG_SENTINEL;
+        if (t0 + tid < p.ng) {
+          kp = p.gidx[t0 + tid];
+          const int dr = kp - r;
+          if (dr >= 0 && dr % dil == 0) kr = dr / dil;
+        }
+        gmeta[0][tid] = kp;
+        gmeta[1][tid] = kr;
+      }
+      tile_commit<T, 256>(tr, st0, st0 + TILEB, tid);
+      __syncthreads();
+      if (wave_live) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          if (t0 + 32 * kh >= p.ng) continue;
+          f32x16 s = score_unit(st0, kh, qf, lane);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kk = 32 * kh + key_of_reg<T>(j, g);
+            const int kp = gmeta[0][kk], kr = gmeta[1][kk];
+            const bool inband = kr >= qi - half && kr <= qi + right;
+            if (!(kp <= lim) || inband) s[j] = -__builtin_inff();
+          }
+          softmax_pv_unit<T>(acc, s, st0 + TILEB, kh, lane, p.c2);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // (2) band tiles through the NS-stage ring: the loads of the next NS-1
+  // tiles are in flight while tile t is computed. Rows past the band end are
+  // clamped to a valid row; their scores are masked, so their values only
+  // ever meet p = 0.
+  const BandWave w{a0, a1, a2, kb, vb, kbeg, kend, nband, r, dil, qi, qw0, half, right, nr,
+                   wk_lo, wk_hi, wave, lane, g, wave_live, p.c2};
+  if (p.ng > 0) {  // the prologue has drained every load; start the ring now
+    dma_tile<T>(a0, kb, vb, kbeg, kend, r, dil, wave, lane);
+    if (NS == 3) dma_tile<T>(a1, kb, vb, kbeg + min(1, nband - 1) * KT, kend, r, dil, wave, lane);
+  }
+  DmaLanes<T> dl;
+  dma_lanes_init<T>(dl, dil, lane);
+  for (int tb = 0; tb < nband; tb += NS) {
+    band_step<T, NS, 0>(tb, acc, qf, w, dl, st0, st1, st2);
+    if (tb + 1 < nband) band_step<T, NS, 1>(tb + 1, acc, qf, w, dl, st0, st1, st2);
+    if (NS == 3 && tb + 2 < nband) band_step<T, NS, NS - 1>(tb + 2, acc, qf, w, dl, st0, st1, st2);
+  }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+
   if (wave_live) {
-    const float ltot = acc.l + wave_xor32(acc.l);
+    const float ltot = pair_sum(acc.l);
     if (row_ok) {
       const float inv = 1.0f / ltot;
       T* orow = reinterpret_cast<T*>(reinterpret_cast<char*>(p.o) + base + (long)pos_q * ROWB);
@@ -478,12 +678,14 @@ __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
 // ----------------------------------------------------------------------------
 // Global rows: partial attention of up to 32 global rows over one key chunk.
 // One wave per workgroup; grid = nsplit * nqb * B*H, split index fastest.
+// Key tiles are double-buffered in LDS so the next tile's loads overlap the
+// current tile's MFMA and softmax work.
 
 template <class T>
 __global__ __launch_bounds__(64) void global_rows_partial(GlobalParams p) {
   constexpr int ROWB = ElemTraits<T>::ROWB;
   constexpr int TILEB = KT * ROWB;
-  __shared__ __attribute__((aligned(16))) char lds[2][TILEB];
+  __shared__ __attribute__((aligned(16))) char lds[2][2][TILEB];
   const int lane = threadIdx.x, g = lane >> 5;
   const int sp = blockIdx.x % p.nsplit;
   const int qb = (blockIdx.x / p.nsplit) % p.nqb;
@@ -493,54 +695,68 @@ __global__ __launch_bounds__(64) void global_rows_partial(GlobalParams p) {
   const char* vb = reinterpret_cast<const char*>(p.vg) + base;
 
   const int gi = qb * 32 + (lane & 31);
-  const int gq = min(gi, p.ng - 1);
-  const int pos_q = p.gidx[gq];
-  // G is sorted: the last row of this block bounds the causal key range.
+  const int pos_q = p.gidx[min(gi, p.ng - 1)];
+  // G is sorted: the first and last rows of this block bound the causal range.
+  const int gmin = p.gidx[min(qb * 32, p.ng - 1)];
   const int gmax = p.gidx[min(qb * 32 + 31, p.ng - 1)];
   const int k_lo = sp * p.ksplit;
   int k_hi = min(p.n, k_lo + p.ksplit);
   if (p.causal) k_hi = min(k_hi, gmax + 1);
   const int lim = p.causal ? pos_q : 0x7fffffff - 1;
+  const int ntile = k_hi > k_lo ? (k_hi - k_lo + KT - 1) / KT : 0;
 
   QFrag<T> qf;
   load_q(qf, reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.qg) + base + (long)pos_q * ROWB), g);
   WaveAcc acc;
   acc_init(acc);
 
-  TileRegs<T, 64> tr;
-  for (int k0 = k_lo; k0 < k_hi; k0 += KT) {
-    PlainRowMap m{k0, k_hi};
-    tile_fetch<T, 64>(tr, kb, vb, m, lane);
-    __syncthreads();
-    tile_commit<T, 64>(tr, lds[0], lds[1], lane);
-    __syncthreads();
-    f32x16 s[2];
-    bool active[2];
+  auto tile = [&](int t, int buf) {
+    const int k0t = k_lo + t * KT;
+#pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int kk0 = k0 + 32 * kh;
-      active[kh] = kk0 < k_hi;
-      if (!active[kh]) continue;
-      s[kh] = score_half(lds[0], kh, qf, lane);
-      const bool interior = kk0 + 31 < k_hi && (!p.causal || kk0 + 31 <= p.gidx[min(qb * 32, p.ng - 1)]);
+      const int kk0 = k0t + 32 * kh;
+      if (kk0 >= k_hi) continue;
+      f32x16 s = score_unit(lds[buf][0], kh, qf, lane);
+      const bool interior = kk0 + 31 < k_hi && (!p.causal || kk0 + 31 <= gmin);
       if (!interior) {
+#pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int kk = kk0 + key_of_reg<T>(j, g);
-          if (kk >= k_hi || !(kk <= lim)) s[kh][j] = -__builtin_inff();
+          if (kk >= k_hi || !(kk <= lim)) s[j] = -__builtin_inff();
         }
       }
+      softmax_pv_unit<T>(acc, s, lds[buf][1], kh, lane, p.c2);
     }
-    softmax_tile<T>(acc, s, active, p.c2);
-    for (int kh = 0; kh < 2; ++kh)
-      if (active[kh]) pv_dispatch<T>(acc, lds[1], kh, s[kh], lane);
-  }
+  };
 
-  const float ltot = acc.l + wave_xor32(acc.l);
+  // All but the last tile: fetch the next tile into registers, compute,
+  // commit. (Fetch and commit are unconditional so that the staging
+  // registers stay in registers.)
+  TileRegs<T, 64> tr;
+  if (ntile > 0) {
+    plain_fetch<T, 64>(tr, kb, vb, k_lo, k_hi, lane);
+    tile_commit<T, 64>(tr, lds[0][0], lds[0][1], lane);
+  }
+  __syncthreads();
+  for (int t = 0; t + 1 < ntile; ++t) {
+    const int buf = t & 1;
+    plain_fetch<T, 64>(tr, kb, vb, k_lo + (t + 1) * KT, k_hi, lane);
+    tile(t, buf);
+    tile_commit<T, 64>(tr, lds[buf ^ 1][0], lds[buf ^ 1][1], lane);
+    __syncthreads();
+  }
+  if (ntile > 0) tile(ntile - 1, (ntile - 1) & 1);
+
+  const float ltot = pair_sum(acc.l);
   if (gi < p.ng) {
     const long slot = ((long)bh * p.ng + gi) * p.nsplit + sp;
     float* po = p.part_o + slot * HD;
+#pragma unroll
     for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
       for (int a = 0; a < 4; ++a) {
         f32x4 t;
+#pragma unroll
         for (int e = 0; e < 4; ++e) t[e] = acc.o[dh][4 * a + e];
         *reinterpret_cast<f32x4*>(po + 32 * dh + 8 * a + 4 * g) = t;
       }
@@ -551,26 +767,53 @@ __global__ __launch_bounds__(64) void global_rows_partial(GlobalParams p) {
   }
 }
 
+constexpr int MAX_SPLIT = 256;
+
+DEV float wave_max(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+DEV float wave_sum(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
 // Log-sum-exp merge of the key chunks of one global row; overwrites O and LSE.
-// One wave per (global row, b*h), grid = ng * B*H; lane = d.
+// One wave per (global row, b*h), grid = ng * B*H. Chunk weights are reduced
+// across lanes; then lane d sums the weighted chunk outputs of column d.
 template <class T>
 __global__ __launch_bounds__(64) void global_rows_merge(GlobalParams p) {
-  const int gi = blockIdx.x % p.ng, bh = blockIdx.x / p.ng, d = threadIdx.x;
+  __shared__ float wts[MAX_SPLIT];
+  const int gi = blockIdx.x % p.ng, bh = blockIdx.x / p.ng, lane = threadIdx.x;
   const long slot0 = ((long)bh * p.ng + gi) * p.nsplit;
+  const float* ml = p.part_ml + slot0 * 2;
   float M = -__builtin_inff();
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.part_ml[(slot0 + s) * 2]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float ms = p.part_ml[(slot0 + s) * 2];
-    if (ms == -__builtin_inff()) continue;
-    const float w = __builtin_amdgcn_exp2f((ms - M) * p.c2);
-    L += w * p.part_ml[(slot0 + s) * 2 + 1];
-    acc += w * p.part_o[(slot0 + s) * HD + d];
+  for (int s = lane; s < p.nsplit; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
+  float L = 0.f;
+  for (int s = lane; s < p.nsplit; s += 64) {
+    const float ms = ml[2 * s];
+    const float w = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((ms - M) * p.c2);
+    wts[s] = w;
+    L += w * ml[2 * s + 1];
   }
+  L = wave_sum(L);
+  __syncthreads();
+  const float* po = p.part_o + slot0 * HD + lane;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = 0;
+  for (; s + 4 <= p.nsplit; s += 4) {
+    a0 += wts[s + 0] * po[(long)(s + 0) * HD];
+    a1 += wts[s + 1] * po[(long)(s + 1) * HD];
+    a2 += wts[s + 2] * po[(long)(s + 2) * HD];
+    a3 += wts[s + 3] * po[(long)(s + 3) * HD];
+  }
+  for (; s < p.nsplit; ++s) a0 += wts[s] * po[(long)s * HD];
+  const float acc = (a0 + a1) + (a2 + a3);
   const int pos = p.gidx[gi];
   T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
-  orow[d] = (T)(acc / L);
-  if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
+  orow[lane] = (T)(acc / L);
+  if (p.lse && lane == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
 }
 
 }  // namespace swattn

@@ -33,11 +33,11 @@ int hip_fail(hipError_t e, const char* what) {
 void choose_split(long bh, int nqb, int n, int* nsplit, int* ksplit) {
   const long target_waves = 2048;
   long want = (target_waves + bh * nqb - 1) / (bh * nqb);
-  const int max_split = (n + KT - 1) / KT;
+  const int max_split = std::min((n + KT - 1) / KT, MAX_SPLIT);
   want = std::max(1L, std::min<long>(want, max_split));
   int ks = (int)(((n + want - 1) / want + KT - 1) / KT) * KT;
   *ksplit = ks;
-  *nsplit = (n + ks - 1) / ks;
+  *nsplit = (n + ks - 1) / ks;  // <= want <= MAX_SPLIT
 }
 
 }  // namespace
