@@ -27,7 +27,7 @@ DEFAULT_WORKLOAD = "encoder_b2_h12_n4096_w512_g1"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "band_fwd_traffic.json")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "attn_fwd_traffic.json")
 KERNEL_SRC = os.path.join(HERE, "sliding_window_attention_banded_amd", "csrc", "kernels.hpp")
 
 
@@ -36,7 +36,7 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload):
-    """HBM bytes per band-kernel launch from committed rocprofv3 counters,
+    """HBM bytes per forward-kernel launch from committed rocprofv3 counters,
     or None when absent or taken on a different kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -112,7 +112,7 @@ def main():
 
     from sliding_window_attention_banded_amd import Plan
     from sliding_window_attention_banded_amd.accounting import (
-        algorithmic_bytes, band_flops, global_column_extras, useful_flops)
+        algorithmic_bytes, band_flops, useful_flops)
     from sliding_window_attention_banded_amd.workloads import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
@@ -168,13 +168,13 @@ def main():
             step(i)
         band_ms, glob_ms, cnt = plan.kernel_times()
         plan.set_timing(False)
-        print(f"[bench] band kernel {band_ms * 1e3:.2f} us, global-row pass "
+        print(f"[bench] forward kernel {band_ms * 1e3:.2f} us, global-row merge "
               f"{glob_ms * 1e3:.2f} us (HIP events, {cnt} launches)", file=sys.stderr, flush=True)
 
     bf = band_flops(wl)
-    extras = sum(int(global_column_extras(wl.n, wl.window[h], wl.dilation[h], wl.causal,
-                                          wl.global_idx).sum()) for h in range(wl.heads))
-    band_kernel_flops = bf + 4 * wl.d * wl.batch * extras
+    # the forward kernel computes the band, the global columns and the global
+    # rows' partials; the merge kernel after it only combines partials
+    band_kernel_flops = useful_flops(wl)
     tokens = wl.batch * wl.n
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     roof = None
@@ -185,13 +185,12 @@ def main():
                 "frac": achieved / peak,
                 "traffic": tr,
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
-                "kernel": "band_fwd", "kernel_us": band_ms * 1e3,
+                "kernel": "attn_fwd", "kernel_us": band_ms * 1e3,
                 "algorithmic_gflop_per_launch": band_kernel_flops / 1e9,
                 "algorithmic_gbytes_per_launch": algorithmic_bytes(wl) / 1e9,
-                "hbm_frac_algorithmic": (4 * wl.batch * wl.heads * wl.n * wl.d *
-                                         (2 if wl.dtype == "bf16" else 4) /
-                                         (band_ms * 1e-3) / 1e9) / PEAK_HBM_GBS,
-                "global_pass_us": glob_ms * 1e3 if glob_ms else 0.0}
+                "hbm_frac_algorithmic": (algorithmic_bytes(wl) / (band_ms * 1e-3) / 1e9)
+                                        / PEAK_HBM_GBS,
+                "merge_us": glob_ms * 1e3 if glob_ms else 0.0}
 
     line = {
         "metric": METRIC,

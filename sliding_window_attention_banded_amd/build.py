@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     # MFMA accumulators in ordinary VGPRs: the softmax reads them directly
     # instead of copying them out of AGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # no NaN canonicalisation in max/min (a NaN input gives a NaN output
+    # either way; infinities are still honoured: masking relies on -inf)
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

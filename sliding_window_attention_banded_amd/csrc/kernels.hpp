@@ -8,7 +8,7 @@
 // Vg. Softmax scale 1/sqrt(64).
 //
 // Work decomposition (all kernels share the wave-level 32-key unit below):
-//  * band_fwd: one workgroup = 4 waves = 128 query rows of one residue class
+//  * band blocks: one workgroup = 4 waves = 128 query rows of one residue class
 //    r (rows r, r+dil, r+2*dil, ... of one (batch, head)); within a residue
 //    class the dilated window is an ordinary window of w+1 keys, so K/V rows
 //    are read with a row stride of dil*64 elements and no key is wasted on
@@ -19,10 +19,11 @@
 //    already inside the band is not counted twice; the running max/sum of
 //    the online softmax merges them with the band exactly as a log-sum-exp
 //    merge would.
-//  * global_rows_partial: rows of G against a chunk of all keys with Qg, Kg,
-//    Vg; writes an unnormalised partial (o, m, l) per chunk.
+//  * global-row blocks: rows of G against a chunk of all keys with Qg, Kg,
+//    Vg, through the same ring; each writes an unnormalised partial (o, m, l)
+//    per chunk. They share one launch (attn_fwd) with the band blocks.
 //  * global_rows_merge: log-sum-exp merge of the chunks; overwrites rows G of
-//    O (and LSE), stream-ordered after band_fwd.
+//    O (and LSE), stream-ordered after attn_fwd.
 //
 // Score tiles are computed transposed, S^T = K Q^T, with the 32x32 MFMA: each
 // lane then owns one query column, so row max and row sum are in-lane
@@ -96,7 +97,8 @@ struct GlobalParams {
   int causal;
   int nsplit;
   int ksplit;   // keys per split, multiple of 64
-  int nqb;      // ceil(ng / 32)
+  int nqb;      // ceil(ng / 32): blocks of 32 global rows
+  int ngroup;   // ceil(nqb / 4): groups of 4 such blocks (one per wave)
   float c2;
   float scale;
 };
@@ -191,8 +193,10 @@ template <> struct QFrag<float> { float v[32]; };   // d = 2s + g
 
 struct WaveAcc {
   f32x16 o[2];
-  float m;
-  float l;
+  float m;     // reference max (raw score units)
+  float l;     // this lane's partial row sum
+  float thr;   // m + RESCALE_LOG2 / c2: a unit max above it raises m
+  float moff;  // -m * c2 (0 while m = -inf): exp2 argument offset
 };
 
 DEV void acc_init(WaveAcc& a) {
@@ -200,6 +204,8 @@ DEV void acc_init(WaveAcc& a) {
   for (int i = 0; i < 16; ++i) { a.o[0][i] = 0.f; a.o[1][i] = 0.f; }
   a.m = -__builtin_inff();
   a.l = 0.f;
+  a.thr = -__builtin_inff();
+  a.moff = 0.f;
 }
 
 // Load the B operand of S^T = K Q^T for this lane's query row (global memory).
@@ -235,20 +241,14 @@ DEV f32x16 score_unit(const char* kbuf, int kh, const QFrag<float>& qf, int lane
   return s;
 }
 
-// O^T += V^T P^T for one 32-key unit whose probabilities are p (accumulator
-// layout of score_unit).
-DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane, __bf16) {
+// O^T += V^T P^T for one 32-key unit; b[sp] holds the bf16 probabilities of
+// keys 16*sp + 8g .. +7 (the B operand, straight from the accumulator layout
+// of score_unit).
+DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const bf16x8 (&b)[2], int lane) {
   const int g = lane >> 5;
   const int i16 = lane & 15;
 #pragma unroll
   for (int sp = 0; sp < 2; ++sp) {
-    bf16x8 b;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 t = __builtin_convertvector(f32x2{p[8 * sp + e], p[8 * sp + e + 1]}, bf16x2);
-      b[e] = t[0];
-      b[e + 1] = t[1];
-    }
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh) {
       // Source lane i16 of each 16-lane group points at 4 d-contiguous
@@ -263,7 +263,7 @@ DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int la
       const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(vbuf + ElemTraits<__bf16>::lds_off(row1, col >> 3) + ((col & 7) << 1)));
       const s16x8 a = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc.o[dh] = mfma_bf16(__builtin_bit_cast(bf16x8, a), b, acc.o[dh]);
+      acc.o[dh] = mfma_bf16(__builtin_bit_cast(bf16x8, a), b[sp], acc.o[dh]);
     }
   }
 }
@@ -291,6 +291,9 @@ template <class T> DEV constexpr int key_of_reg(int j, int g) {
 // the stale m stay below 2^RESCALE_LOG2, which fp32 accumulators and the bf16
 // P operand hold without loss of relative precision. O = acc / l and
 // LSE = m*scale + ln l are the same quantities as with an exact running max.
+// In bf16 the row sum l is the sum of the bf16-rounded weights, so O is an
+// exact convex combination of V rows up to fp32 rounding, and LSE carries at
+// most the 2^-8 relative rounding of a weight.
 constexpr float RESCALE_LOG2 = 8.0f;
 
 template <class T>
@@ -298,29 +301,48 @@ DEV void softmax_pv_unit(WaveAcc& acc, f32x16 s, const char* vbuf, int kh, int l
   float mx = s[0];
 #pragma unroll
   for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
-  const float thr = acc.m * c2 + RESCALE_LOG2;
-  if (__builtin_amdgcn_ballot_w64(mx * c2 > thr)) {
+  if (__builtin_amdgcn_ballot_w64(mx > acc.thr)) {
     const float pm = pair_max(mx);
-    const bool upd = pm * c2 > thr;  // the same decision on both lanes of a row
+    const bool upd = pm > acc.thr;  // the same decision on both lanes of a row
     // rows that do not move keep alpha = 1 (also while their m is still -inf)
     const float alpha = upd ? __builtin_amdgcn_exp2f((acc.m - pm) * c2) : 1.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc.o[0][i] *= alpha; acc.o[1][i] *= alpha; }
     acc.l *= alpha;
     acc.m = upd ? pm : acc.m;
+    acc.thr = acc.m + RESCALE_LOG2 / c2;
+    // a row with every key masked so far has m = -inf and only -inf scores
+    acc.moff = acc.m == -__builtin_inff() ? 0.f : -acc.m * c2;
   }
-  // a row with every key masked so far has m = -inf and only -inf scores
-  const float moff = acc.m == -__builtin_inff() ? 0.f : -acc.m * c2;
-  float l0 = 0.f, l1 = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    // P in bf16 (round to nearest even) is the MFMA operand; the row sum adds
+    // up exactly these rounded weights, two at a time.
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8 b[2];
+    float l = acc.l;
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, moff));
-    s[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, moff));
-    l0 += s[j];
-    l1 += s[j + 1];
+    for (int j = 0; j < 16; j += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
+      const bf16x2 t = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+      l = __builtin_amdgcn_fdot2_f32_bf16(t, one, l, false);
+      b[j >> 3][j & 7] = t[0];
+      b[j >> 3][(j & 7) + 1] = t[1];
+    }
+    acc.l = l;
+    pv_unit(acc, vbuf, kh, b, lane);
+  } else {
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
+      s[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
+      l0 += s[j];
+      l1 += s[j + 1];
+    }
+    acc.l += l0 + l1;
+    pv_unit(acc, vbuf, kh, s, lane, T{});
   }
-  acc.l += l0 + l1;
-  pv_unit(acc, vbuf, kh, s, lane, T{});
 }
 
 // Mask one 32-key unit of a band tile: key kk = k0 + key_of_reg(j, g) is
@@ -484,19 +506,46 @@ DEV void plain_fetch(TileRegs<T, NT>& tr, const char* kb, const char* vb, int kb
 }
 
 // ----------------------------------------------------------------------------
-// Band kernel (with the global columns folded in as extra key tiles).
+// The key-tile ring shared by band blocks and global-row blocks.
 
-// Per-wave constants of the band loop.
-struct BandWave {
+// Key side of a ring pass: tiles of 64 rows r + kk*dil, kk = kbeg + 64t,
+// clamped to kend - 1, in LDS stages at a0/a1/a2.
+struct RingCtx {
   unsigned a0, a1, a2;  // LDS byte addresses of the stages (a2 unused with 2)
-  const char* kb;  // K rows of this (batch, head)
-  const char* vb;  // V rows of this (batch, head)
-  int kbeg, kend, nband;  // key tiles: rows kbeg + 64t, clamped to kend - 1
-  int r, dil;
-  int qi, qw0, half, right, nr, wk_lo, wk_hi;
+  const char* kb;       // K rows of this (batch, head)
+  const char* vb;       // V rows of this (batch, head)
+  int kbeg, kend, nband, r, dil;
   int wave, lane, g;
-  bool live;
+  bool live;            // this wave has query rows to compute
   float c2;
+};
+
+// Which 32-key units a band wave computes and how they are masked: row qi
+// sees keys qi - half .. qi + right of its residue class, clipped to nr.
+struct BandPol {
+  int qi, qw0, half, right, nr, wk_lo, wk_hi;
+  DEV bool active(int ku) const { return ku <= wk_hi && ku + 31 >= wk_lo; }
+  DEV bool interior(int ku) const {
+    return ku >= qw0 + 31 - half && ku + 31 <= qw0 + right && ku + 31 < nr;
+  }
+  template <class T> DEV void mask(f32x16& s, int ku, int g) const {
+    mask_band_unit<T>(s, ku, qi, half, right, nr, g);
+  }
+};
+
+// Global rows against a contiguous chunk of keys [.., k_hi): every key below
+// k_hi, and left of the row when causal (lim = the row's position).
+struct GlobPol {
+  int lim, k_hi, gmin, causal;
+  DEV bool active(int ku) const { return ku < k_hi; }
+  DEV bool interior(int ku) const { return ku + 31 < k_hi && (!causal || ku + 31 <= gmin); }
+  template <class T> DEV void mask(f32x16& s, int ku, int g) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = ku + key_of_reg<T>(j, g);
+      if (kk >= k_hi || kk > lim) s[j] = -__builtin_inff();
+    }
+  }
 };
 
 // One step of the NS-stage ring (NS = 2 or 3) for tile tb, which sits in
@@ -507,55 +556,75 @@ struct BandWave {
 // depend on the loads in flight to the others. Every step issues exactly one
 // tile of DMA (past the last tile it re-fetches the last tile into a stage
 // nobody reads again), so every step's wait has the same count.
-template <class T, int NS, int S>
-DEV void band_step(int tb, WaveAcc& acc, const QFrag<T>& qf, const BandWave& w,
+template <class T, int NS, int S, class Pol>
+DEV void ring_step(int tb, WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, const Pol& pol,
                    const DmaLanes<T>& dl, const char* st0, const char* st1, const char* st2) {
   constexpr int TILEB = KT * ElemTraits<T>::ROWB;
   const char* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
   constexpr int SN = (S + NS - 1) % NS;
-  const unsigned nxt = SN == 0 ? w.a0 : (SN == 1 ? w.a1 : w.a2);
+  const unsigned nxt = SN == 0 ? c.a0 : (SN == 1 ? c.a1 : c.a2);
   wait_vmcnt<NS == 3 ? Dma<T>::PER_WAVE : 0>();
   wg_barrier();  // tile tb has landed for every wave; tile tb-1 is consumed
-  const int kn = w.kbeg + min(tb + NS - 1, w.nband - 1) * KT;
-  if (kn + KT <= w.kend) dma_tile_fast<T>(nxt, dl, w.kb, w.vb, kn, w.r, w.dil, w.wave);
-  else dma_tile<T>(nxt, w.kb, w.vb, kn, w.kend, w.r, w.dil, w.wave, w.lane);
-  if (!w.live) return;
-  const int k0 = w.kbeg + tb * KT;
+  const int kn = c.kbeg + min(tb + NS - 1, c.nband - 1) * KT;
+  if (kn + KT <= c.kend) dma_tile_fast<T>(nxt, dl, c.kb, c.vb, kn, c.r, c.dil, c.wave);
+  else dma_tile<T>(nxt, c.kb, c.vb, kn, c.kend, c.r, c.dil, c.wave, c.lane);
+  if (!c.live) return;
+  const int k0 = c.kbeg + tb * KT;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const int ku = k0 + 32 * kh;
-    if (ku > w.wk_hi || ku + 31 < w.wk_lo) continue;  // wave-uniform skip
-    f32x16 sc = score_unit(cur, kh, qf, w.lane);
-    const bool interior = ku >= w.qw0 + 31 - w.half && ku + 31 <= w.qw0 + w.right && ku + 31 < w.nr;
-    if (!interior) mask_band_unit<T>(sc, ku, w.qi, w.half, w.right, w.nr, w.g);
-    softmax_pv_unit<T>(acc, sc, cur + TILEB, kh, w.lane, w.c2);
+    if (!pol.active(ku)) continue;  // wave-uniform skip
+    f32x16 sc = score_unit(cur, kh, qf, c.lane);
+    if (!pol.interior(ku)) pol.template mask<T>(sc, ku, c.g);
+    softmax_pv_unit<T>(acc, sc, cur + TILEB, kh, c.lane, c.c2);
   }
 }
 
-// LDS ring depth of the band kernel and the resulting waves per SIMD: bf16
-// tiles are 16 KB (K + V), so three stages (48 KB) leave room for three
-// workgroups per CU; fp32 tiles are 32 KB.
-template <class T> struct BandCfg;
-template <> struct BandCfg<__bf16> { static constexpr int NS = 3; };
-template <> struct BandCfg<float> { static constexpr int NS = 2; };
+// LDS ring depth and resulting waves per SIMD: bf16 tiles are 16 KB (K + V),
+// so three stages (48 KB) leave room for three workgroups per CU; fp32 tiles
+// are 32 KB.
+template <class T> struct RingCfg;
+template <> struct RingCfg<__bf16> { static constexpr int NS = 3; };
+template <> struct RingCfg<float> { static constexpr int NS = 2; };
+
+// Start the ring: DMA of tile 0 (and 1 with three stages).
+template <class T>
+DEV void ring_start(const RingCtx& c) {
+  dma_tile<T>(c.a0, c.kb, c.vb, c.kbeg, c.kend, c.r, c.dil, c.wave, c.lane);
+  if (RingCfg<T>::NS == 3)
+    dma_tile<T>(c.a1, c.kb, c.vb, c.kbeg + min(1, c.nband - 1) * KT, c.kend, c.r, c.dil, c.wave, c.lane);
+}
+
+// Run every tile of the ring (ring_start has been issued and, with it, any
+// earlier loads of this wave waited for).
+template <class T, class Pol>
+DEV void ring_run(WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, const Pol& pol,
+                  const char* st0, const char* st1, const char* st2) {
+  constexpr int NS = RingCfg<T>::NS;
+  DmaLanes<T> dl;
+  dma_lanes_init<T>(dl, c.dil, c.lane);
+  for (int tb = 0; tb < c.nband; tb += NS) {
+    ring_step<T, NS, 0>(tb, acc, qf, c, pol, dl, st0, st1, st2);
+    if (tb + 1 < c.nband) ring_step<T, NS, 1>(tb + 1, acc, qf, c, pol, dl, st0, st1, st2);
+    if (NS == 3 && tb + 2 < c.nband) ring_step<T, NS, NS - 1>(tb + 2, acc, qf, c, pol, dl, st0, st1, st2);
+  }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+}
+
+// ----------------------------------------------------------------------------
+// Band block: 128 query rows of one residue class, with the global columns
+// folded in as extra key tiles.
 
 template <class T>
-__global__ __launch_bounds__(256) void band_fwd(BandParams p) {
+DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* st2, int (*gmeta)[KT]) {
   constexpr int ROWB = ElemTraits<T>::ROWB;
   constexpr int CPR = ElemTraits<T>::CPR;
   constexpr int TILEB = KT * ROWB;
-  constexpr int STAGEB = 2 * TILEB;
-  __shared__ __attribute__((aligned(1024))) char st0[STAGEB];
-  __shared__ __attribute__((aligned(1024))) char st1[STAGEB];
-  constexpr int NS = BandCfg<T>::NS;
-  __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGEB : 1024];
-  __shared__ int gmeta[2][KT];  // global tile: key position, residue-local index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int4 td = p.tiles[bid];
+  const int4 td = p.tiles[tile];
   const int bh = td.x, r = td.y, q0 = td.z;
   const HeadInfo hi = p.heads[bh % p.H];
   const int half = hi.half, right = hi.right, dil = hi.dil;
@@ -577,19 +646,19 @@ __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
   const int wk_lo = max(0, qw0 - half);
   const int wk_hi = min(nr - 1, qw0 + 31 + right);
 
-  const unsigned a0 = (unsigned)(uintptr_t)(lds_void*)st0;
-  const unsigned a1 = (unsigned)(uintptr_t)(lds_void*)st1;
-  const unsigned a2 = (unsigned)(uintptr_t)(lds_void*)st2;
+  const RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+                  (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
+                  wave, lane, g, wave_live, p.c2};
+  const BandPol pol{qi, qw0, half, right, nr, wk_lo, wk_hi};
   const T* qrow = reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.q) + base + (long)pos_q * ROWB);
   QFrag<T> qf;
   WaveAcc acc;
   acc_init(acc);
   if (p.ng == 0) {
-    // start the first two band tiles, then Q; one wait covers all of them
-    // (the compiler must not see Q in flight inside the band loop, where it
-    // does not know about the tile loads)
-    dma_tile<T>(a0, kb, vb, kbeg, kend, r, dil, wave, lane);
-    if (NS == 3) dma_tile<T>(a1, kb, vb, kbeg + min(1, nband - 1) * KT, kend, r, dil, wave, lane);
+    // start the first band tiles, then Q; one wait covers all of them (the
+    // compiler must not see Q in flight inside the ring, where it does not
+    // know about the tile loads)
+    ring_start<T>(c);
     load_q(qf, qrow, g);
     wait_vmcnt<0>();
   } else {
@@ -643,26 +712,13 @@ __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
       }
       __syncthreads();
     }
+    ring_start<T>(c);  // the prologue has drained every load; start the ring now
   }
 
-  // (2) band tiles through the NS-stage ring: the loads of the next NS-1
-  // tiles are in flight while tile t is computed. Rows past the band end are
-  // clamped to a valid row; their scores are masked, so their values only
-  // ever meet p = 0.
-  const BandWave w{a0, a1, a2, kb, vb, kbeg, kend, nband, r, dil, qi, qw0, half, right, nr,
-                   wk_lo, wk_hi, wave, lane, g, wave_live, p.c2};
-  if (p.ng > 0) {  // the prologue has drained every load; start the ring now
-    dma_tile<T>(a0, kb, vb, kbeg, kend, r, dil, wave, lane);
-    if (NS == 3) dma_tile<T>(a1, kb, vb, kbeg + min(1, nband - 1) * KT, kend, r, dil, wave, lane);
-  }
-  DmaLanes<T> dl;
-  dma_lanes_init<T>(dl, dil, lane);
-  for (int tb = 0; tb < nband; tb += NS) {
-    band_step<T, NS, 0>(tb, acc, qf, w, dl, st0, st1, st2);
-    if (tb + 1 < nband) band_step<T, NS, 1>(tb + 1, acc, qf, w, dl, st0, st1, st2);
-    if (NS == 3 && tb + 2 < nband) band_step<T, NS, NS - 1>(tb + 2, acc, qf, w, dl, st0, st1, st2);
-  }
-  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
+  // (2) band tiles through the ring: the loads of the next tiles are in
+  // flight while tile t is computed. Rows past the band end are clamped to a
+  // valid row; their scores are masked, so their values only ever meet p = 0.
+  ring_run<T>(acc, qf, c, pol, st0, st1, st2);
 
   if (wave_live) {
     const float ltot = pair_sum(acc.l);
@@ -676,144 +732,145 @@ __global__ __launch_bounds__(256) void band_fwd(BandParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// Global rows: partial attention of up to 32 global rows over one key chunk.
-// One wave per workgroup; grid = nsplit * nqb * B*H, split index fastest.
-// Key tiles are double-buffered in LDS so the next tile's loads overlap the
-// current tile's MFMA and softmax work.
+// Global-row block: up to 4 x 32 global rows (one block of 32 per wave)
+// against one chunk of keys of Kg, Vg; writes an unnormalised partial
+// (o, m, l) per row and chunk. Block index = split + nsplit*(group +
+// ngroup*bh).
 
 template <class T>
-__global__ __launch_bounds__(64) void global_rows_partial(GlobalParams p) {
+DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char* st2) {
   constexpr int ROWB = ElemTraits<T>::ROWB;
-  constexpr int TILEB = KT * ROWB;
-  __shared__ __attribute__((aligned(16))) char lds[2][2][TILEB];
-  const int lane = threadIdx.x, g = lane >> 5;
-  const int sp = blockIdx.x % p.nsplit;
-  const int qb = (blockIdx.x / p.nsplit) % p.nqb;
-  const int bh = blockIdx.x / (p.nsplit * p.nqb);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sp = gb % p.nsplit;
+  const int grp = (gb / p.nsplit) % p.ngroup;
+  const int bh = gb / (p.nsplit * p.ngroup);
   const long base = (long)bh * p.n * ROWB;
-  const char* kb = reinterpret_cast<const char*>(p.kg) + base;
-  const char* vb = reinterpret_cast<const char*>(p.vg) + base;
 
+  const int qb = grp * BAND_WAVES + wave;  // this wave's block of 32 global rows
+  const bool live = qb < p.nqb;
   const int gi = qb * 32 + (lane & 31);
   const int pos_q = p.gidx[min(gi, p.ng - 1)];
-  // G is sorted: the first and last rows of this block bound the causal range.
+  // G is sorted: the first row of the wave and the last row of the group
+  // bound the causal key ranges.
   const int gmin = p.gidx[min(qb * 32, p.ng - 1)];
-  const int gmax = p.gidx[min(qb * 32 + 31, p.ng - 1)];
+  const int gmax = p.gidx[min(grp * BAND_WAVES * 32 + BAND_WAVES * 32 - 1, p.ng - 1)];
   const int k_lo = sp * p.ksplit;
   int k_hi = min(p.n, k_lo + p.ksplit);
   if (p.causal) k_hi = min(k_hi, gmax + 1);
-  const int lim = p.causal ? pos_q : 0x7fffffff - 1;
-  const int ntile = k_hi > k_lo ? (k_hi - k_lo + KT - 1) / KT : 0;
+  const int nband = k_hi > k_lo ? (k_hi - k_lo + KT - 1) / KT : 0;  // workgroup-uniform
 
+  const RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+                  (unsigned)(uintptr_t)(lds_void*)st2,
+                  reinterpret_cast<const char*>(p.kg) + base, reinterpret_cast<const char*>(p.vg) + base,
+                  k_lo, k_hi, nband, 0, 1, wave, lane, g, live, p.c2};
+  const GlobPol pol{p.causal ? pos_q : 0x7fffffff - 1, k_hi, gmin, p.causal};
   QFrag<T> qf;
-  load_q(qf, reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.qg) + base + (long)pos_q * ROWB), g);
   WaveAcc acc;
   acc_init(acc);
+  if (nband > 0) {
+    ring_start<T>(c);
+    load_q(qf, reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.qg) + base + (long)pos_q * ROWB), g);
+    wait_vmcnt<0>();
+    ring_run<T>(acc, qf, c, pol, st0, st1, st2);
+  }
 
-  auto tile = [&](int t, int buf) {
-    const int k0t = k_lo + t * KT;
+  if (live) {
+    const float ltot = pair_sum(acc.l);
+    if (gi < p.ng) {
+      const long slot = ((long)bh * p.ng + gi) * p.nsplit + sp;
+      float* po = p.part_o + slot * HD;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int kk0 = k0t + 32 * kh;
-      if (kk0 >= k_hi) continue;
-      f32x16 s = score_unit(lds[buf][0], kh, qf, lane);
-      const bool interior = kk0 + 31 < k_hi && (!p.causal || kk0 + 31 <= gmin);
-      if (!interior) {
+      for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kk = kk0 + key_of_reg<T>(j, g);
-          if (kk >= k_hi || !(kk <= lim)) s[j] = -__builtin_inff();
+        for (int a = 0; a < 4; ++a) {
+          f32x4 t;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[e] = acc.o[dh][4 * a + e];
+          *reinterpret_cast<f32x4*>(po + 32 * dh + 8 * a + 4 * g) = t;
         }
+      if (g == 0) {
+        p.part_ml[slot * 2 + 0] = acc.m;
+        p.part_ml[slot * 2 + 1] = ltot;
       }
-      softmax_pv_unit<T>(acc, s, lds[buf][1], kh, lane, p.c2);
     }
-  };
-
-  // All but the last tile: fetch the next tile into registers, compute,
-  // commit. (Fetch and commit are unconditional so that the staging
-  // registers stay in registers.)
-  TileRegs<T, 64> tr;
-  if (ntile > 0) {
-    plain_fetch<T, 64>(tr, kb, vb, k_lo, k_hi, lane);
-    tile_commit<T, 64>(tr, lds[0][0], lds[0][1], lane);
   }
-  __syncthreads();
-  for (int t = 0; t + 1 < ntile; ++t) {
-    const int buf = t & 1;
-    plain_fetch<T, 64>(tr, kb, vb, k_lo + (t + 1) * KT, k_hi, lane);
-    tile(t, buf);
-    tile_commit<T, 64>(tr, lds[buf ^ 1][0], lds[buf ^ 1][1], lane);
-    __syncthreads();
-  }
-  if (ntile > 0) tile(ntile - 1, (ntile - 1) & 1);
+}
 
-  const float ltot = pair_sum(acc.l);
-  if (gi < p.ng) {
-    const long slot = ((long)bh * p.ng + gi) * p.nsplit + sp;
-    float* po = p.part_o + slot * HD;
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        f32x4 t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = acc.o[dh][4 * a + e];
-        *reinterpret_cast<f32x4*>(po + 32 * dh + 8 * a + 4 * g) = t;
-      }
-    if (g == 0) {
-      p.part_ml[slot * 2 + 0] = acc.m;
-      p.part_ml[slot * 2 + 1] = ltot;
-    }
+// ----------------------------------------------------------------------------
+// The forward kernel: blocks [0, nglob_blocks) are global-row blocks (padded
+// to a multiple of 8 so that the XCD order of the band blocks is unchanged),
+// the rest band blocks. Listing the memory-bound global-row blocks first lets
+// them stream Kg/Vg while the compute-bound band blocks run beside them.
+
+template <class T>
+__global__ __launch_bounds__(256) void attn_fwd(BandParams bp, GlobalParams gp, int nglob_blocks,
+                                                int nglob_real) {
+  constexpr int STAGEB = 2 * KT * ElemTraits<T>::ROWB;
+  constexpr int NS = RingCfg<T>::NS;
+  __shared__ __attribute__((aligned(1024))) char st0[STAGEB];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGEB];
+  __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGEB : 1024];
+  __shared__ int gmeta[2][KT];  // global-column tile: key position, residue-local index
+  const int b = blockIdx.x;
+  if (b < nglob_blocks) {
+    if (b < nglob_real) global_block<T>(gp, b, st0, st1, st2);
+  } else {
+    band_block<T>(bp, xcd_remap(b - nglob_blocks, gridDim.x - nglob_blocks), st0, st1, st2, gmeta);
   }
 }
 
 constexpr int MAX_SPLIT = 256;
 
-DEV float wave_max(float x) {
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
-}
-DEV float wave_sum(float x) {
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+// Log-sum-exp merge of the key chunks of one global row; overwrites O and LSE.
+// One 256-thread block per (global row, b*h), grid = ng * B*H. Thread t owns
+// column t%64 of chunks t/64, t/64 + 4, ...; it loads them in batches of 8
+// (all loads of a batch in flight at once) and folds them into a running
+// (max, sum, output); the four groups are then folded the same way in LDS.
+DEV void lse_fold(float& M, float& L, float& A, float m, float l, float a, float c2) {
+  const float mn = fmaxf(M, m);
+  const float fo = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((M - mn) * c2);
+  const float fn = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+  L = L * fo + l * fn;
+  A = A * fo + a * fn;
+  M = mn;
 }
 
-// Log-sum-exp merge of the key chunks of one global row; overwrites O and LSE.
-// One wave per (global row, b*h), grid = ng * B*H. Chunk weights are reduced
-// across lanes; then lane d sums the weighted chunk outputs of column d.
 template <class T>
-__global__ __launch_bounds__(64) void global_rows_merge(GlobalParams p) {
-  __shared__ float wts[MAX_SPLIT];
-  const int gi = blockIdx.x % p.ng, bh = blockIdx.x / p.ng, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
+  __shared__ float sm[4][HD], sl[4][HD], sa[4][HD];
+  const int gi = blockIdx.x % p.ng, bh = blockIdx.x / p.ng, tid = threadIdx.x;
+  const int d = tid & 63, grp = tid >> 6;
   const long slot0 = ((long)bh * p.ng + gi) * p.nsplit;
   const float* ml = p.part_ml + slot0 * 2;
-  float M = -__builtin_inff();
-  for (int s = lane; s < p.nsplit; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int s = lane; s < p.nsplit; s += 64) {
-    const float ms = ml[2 * s];
-    const float w = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((ms - M) * p.c2);
-    wts[s] = w;
-    L += w * ml[2 * s + 1];
+  const float* po = p.part_o + slot0 * HD + d;
+  float M = -__builtin_inff(), L = 0.f, A = 0.f;
+  for (int b0 = grp; b0 < p.nsplit; b0 += 32) {
+    float m[8], l[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sidx = b0 + 4 * i;
+      const bool ok = sidx < p.nsplit;
+      m[i] = ok ? ml[2 * sidx] : -__builtin_inff();
+      l[i] = ok ? ml[2 * sidx + 1] : 0.f;
+      o[i] = ok ? po[(long)sidx * HD] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lse_fold(M, L, A, m[i], l[i], o[i], p.c2);
   }
-  L = wave_sum(L);
+  sm[grp][d] = M;
+  sl[grp][d] = L;
+  sa[grp][d] = A;
   __syncthreads();
-  const float* po = p.part_o + slot0 * HD + lane;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int s = 0;
-  for (; s + 4 <= p.nsplit; s += 4) {
-    a0 += wts[s + 0] * po[(long)(s + 0) * HD];
-    a1 += wts[s + 1] * po[(long)(s + 1) * HD];
-    a2 += wts[s + 2] * po[(long)(s + 2) * HD];
-    a3 += wts[s + 3] * po[(long)(s + 3) * HD];
+  if (tid < HD) {
+#pragma unroll
+    for (int q = 1; q < 4; ++q) lse_fold(M, L, A, sm[q][d], sl[q][d], sa[q][d], p.c2);
+    const int pos = p.gidx[gi];
+    T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
+    orow[d] = (T)(A / L);
+    if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
   }
-  for (; s < p.nsplit; ++s) a0 += wts[s] * po[(long)s * HD];
-  const float acc = (a0 + a1) + (a2 + a3);
-  const int pos = p.gidx[gi];
-  T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
-  orow[lane] = (T)(acc / L);
-  if (p.lse && lane == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
 }
 
 }  // namespace swattn

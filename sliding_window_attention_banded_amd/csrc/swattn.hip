@@ -28,16 +28,14 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SWATTN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Global-row pass: number of key chunks per (row block, b*h). Enough chunks
-// to put a few thousand waves in flight; each chunk a multiple of 64 keys.
-void choose_split(long bh, int nqb, int n, int* nsplit, int* ksplit) {
-  const long target_waves = 2048;
-  long want = (target_waves + bh * nqb - 1) / (bh * nqb);
-  const int max_split = std::min((n + KT - 1) / KT, MAX_SPLIT);
-  want = std::max(1L, std::min<long>(want, max_split));
-  int ks = (int)(((n + want - 1) / want + KT - 1) / KT) * KT;
+// Global-row pass: keys are cut into chunks of ksplit (a multiple of 64,
+// about four tiles) so that every (b*h, group of 128 global rows) yields a
+// few independent blocks; at most MAX_SPLIT chunks.
+void choose_split(int n, int* nsplit, int* ksplit) {
+  int ks = 4 * KT;
+  while ((n + ks - 1) / ks > MAX_SPLIT) ks += KT;
   *ksplit = ks;
-  *nsplit = (n + ks - 1) / ks;  // <= want <= MAX_SPLIT
+  *nsplit = (n + ks - 1) / ks;
 }
 
 }  // namespace
@@ -45,7 +43,7 @@ void choose_split(long bh, int nqb, int n, int* nsplit, int* ksplit) {
 struct swattn_plan {
   int B, H, n, d, causal, ng, dtype, device;
   int ntiles;
-  int nsplit, ksplit, nqb;
+  int nsplit, ksplit, nqb, ngroup, nglob_blocks, nglob_real;
   void* dev_mem;          // one allocation, carved below
   HeadInfo* heads;        // [H]
   int4* tiles;            // [ntiles]
@@ -99,8 +97,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   if (p->dtype != SWATTN_BF16 && p->dtype != SWATTN_FP32) return fail(SWATTN_ERR_UNSUPPORTED, "unknown dtype");
   const long bh = (long)p->batch * p->heads;
   if (bh * p->n > (1L << 31)) return fail(SWATTN_ERR_UNSUPPORTED, "batch*heads*n must be <= 2^31");
-  // The global-row grid has max(~2048, ceil(|G|/32) * B*H) blocks (see
-  // choose_split) and the merge grid |G| * B*H <= B*H*n: both fit in 2^31.
+  // The merge grid has |G| * B*H <= B*H*n <= 2^31 blocks; the forward grid
+  // is checked below.
 
   // per-head table; a window or dilation beyond n behaves as if clipped to n
   std::vector<HeadInfo> heads(p->heads);
@@ -127,8 +125,20 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->causal = p->causal; pl->ng = p->n_global; pl->dtype = p->dtype;
   pl->ntiles = (int)tiles.size();
   pl->nqb = (pl->ng + 31) / 32;
+  pl->ngroup = (pl->nqb + BAND_WAVES - 1) / BAND_WAVES;
   pl->nsplit = pl->ksplit = 0;
-  if (pl->ng > 0) choose_split(bh, pl->nqb, p->n, &pl->nsplit, &pl->ksplit);
+  pl->nglob_real = pl->nglob_blocks = 0;
+  if (pl->ng > 0) {
+    choose_split(p->n, &pl->nsplit, &pl->ksplit);
+    const long real = (long)pl->nsplit * pl->ngroup * bh;
+    const long padded = (real + 7) / 8 * 8;
+    if (padded + (long)tiles.size() > 0x7fffffffL) {
+      delete pl;
+      return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+    }
+    pl->nglob_real = (int)real;
+    pl->nglob_blocks = (int)padded;
+  }
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
 
@@ -233,28 +243,27 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   bp.tiles = pl->tiles; bp.heads = pl->heads; bp.gidx = pl->gidx; bp.ng = pl->ng;
   bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
   bp.c2 = scale * LOG2E; bp.scale = scale;
+  GlobalParams gp;
+  gp.qg = qg; gp.kg = kg; gp.vg = vg; gp.o = o; gp.lse = lse; gp.gidx = pl->gidx;
+  gp.part_o = pl->part_o; gp.part_ml = pl->part_ml;
+  gp.ng = pl->ng; gp.n = pl->n; gp.causal = pl->causal;
+  gp.nsplit = pl->nsplit; gp.ksplit = pl->ksplit; gp.nqb = pl->nqb; gp.ngroup = pl->ngroup;
+  gp.c2 = scale * LOG2E; gp.scale = scale;
+
   const bool timed = !pl->ev.empty() && pl->ntimed < swattn_plan::kMaxTimed;
   hipEvent_t* ev = timed ? &pl->ev[4 * (size_t)pl->ntimed] : nullptr;
   if (timed) pl->ntimed++;
   hipError_t e = hipSuccess;
   if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  hipLaunchKernelGGL(band_fwd<T>, dim3(pl->ntiles), dim3(256), 0, st, bp);
+  hipLaunchKernelGGL(attn_fwd<T>, dim3(pl->nglob_blocks + pl->ntiles), dim3(256), 0, st, bp, gp,
+                     pl->nglob_blocks, pl->nglob_real);
   e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch band_fwd");
+  if (e != hipSuccess) return hip_fail(e, "launch attn_fwd");
   if (timed && (e = hipEventRecord(ev[1], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (pl->ng > 0) {
     if (timed && (e = hipEventRecord(ev[2], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    GlobalParams gp;
-    gp.qg = qg; gp.kg = kg; gp.vg = vg; gp.o = o; gp.lse = lse; gp.gidx = pl->gidx;
-    gp.part_o = pl->part_o; gp.part_ml = pl->part_ml;
-    gp.ng = pl->ng; gp.n = pl->n; gp.causal = pl->causal;
-    gp.nsplit = pl->nsplit; gp.ksplit = pl->ksplit; gp.nqb = pl->nqb;
-    gp.c2 = scale * LOG2E; gp.scale = scale;
     const int bh = pl->B * pl->H;
-    hipLaunchKernelGGL(global_rows_partial<T>, dim3(pl->nsplit * pl->nqb * bh), dim3(64), 0, st, gp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "launch global_rows_partial");
-    hipLaunchKernelGGL(global_rows_merge<T>, dim3(pl->ng * bh), dim3(64), 0, st, gp);
+    hipLaunchKernelGGL(global_rows_merge<T>, dim3(pl->ng * bh), dim3(256), 0, st, gp);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch global_rows_merge");
     if (timed && (e = hipEventRecord(ev[3], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");

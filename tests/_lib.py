@@ -48,8 +48,11 @@ def oracle_ref(wl, inp, rows=None):
 
 
 # Tolerances. bf16 I/O with fp32 accumulation: max-abs 2e-2 on O, plus a
-# relative RMS bound; LSE within 1e-3. fp32 path: 1e-5 on O and LSE.
-TOL = {"bf16": dict(o=2e-2, rel=1e-2, lse=1e-3),
+# relative RMS bound. The bf16 row sum adds the bf16-rounded weights; round
+# to nearest in bf16 (8 significant bits) is within a relative 2^-8 of the
+# exact weight, so ln(sum) is within 2^-8 = 3.9e-3 of the exact LSE: bound
+# 4e-3. fp32 path: 1e-5 on O and LSE.
+TOL = {"bf16": dict(o=2e-2, rel=1e-2, lse=4e-3),
        "fp32": dict(o=1e-5, rel=2e-6, lse=1e-5)}
 
 
