@@ -59,7 +59,11 @@ constexpr int BM = 32 * BAND_WAVES;  // query rows per band workgroup
 constexpr int NEG_SENTINEL = -(1 << 30);
 constexpr float LOG2E = 1.4426950408889634f;
 
-struct HeadInfo {
+// One band workgroup: (batch*head, residue class r, first residue-local
+// query row q0, rows nr of the residue class) and the head's band geometry,
+// read with one 32-byte scalar load.
+struct TileRec {
+  int bh, r, q0, nr;
   int half;   // w/2, clipped to n
   int right;  // 0 when causal, else half
   int dil;    // dilation, clipped to n
@@ -72,8 +76,11 @@ struct BandParams {
   const void* v;
   void* o;
   float* lse;
-  const int4* tiles;     // {b*H + h, residue r, first residue-local row, 0}
-  const HeadInfo* heads; // [H]
+  // band workgroups: an explicit list, or NULL when every head has the same
+  // geometry (uni_*): then block b is (bh, r, q-block) = b in mixed radix
+  // (B*H, uni_dil, uni_nqb)
+  const TileRec* tiles;
+  int uni_half, uni_right, uni_dil, uni_nqb;
   const int* gidx;       // sorted G, [ng]
   int ng;
   int H;
@@ -277,6 +284,15 @@ DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int la
   }
 }
 
+// key_of_reg(j, g) = key_reg_base(j) + g * key_g_step: masks compare against
+// bounds shifted by the lane's group, so the per-register offsets stay
+// immediates instead of occupying VGPRs.
+template <class T> DEV constexpr int key_reg_base(int j) {
+  if constexpr (sizeof(T) == 2) return ((j >> 3) << 4) + (j & 7);
+  else return 2 * j;
+}
+template <class T> constexpr int key_g_step = sizeof(T) == 2 ? 8 : 1;
+
 template <class T> DEV constexpr int key_of_reg(int j, int g) {
   if constexpr (sizeof(T) == 2) return key_of_reg16(j, g);
   else return key_of_reg32(j, g);
@@ -345,15 +361,113 @@ DEV void softmax_pv_unit(WaveAcc& acc, f32x16 s, const char* vbuf, int kh, int l
   }
 }
 
+// Pieces of a 32-key unit for the software-pipelined ring: fragments are
+// loaded from LDS well before they are used.
+struct KFrag { bf16x8 v[4]; };      // A operand of S^T, 4 k-steps of 16 d
+struct VFrag { bf16x8 a[2][2]; };   // A operand of O^T, [16-key step][d half]
+struct PFrag { bf16x8 b[2]; };      // B operand of O^T, [16-key step]
+
+// Lane-dependent byte offsets of the bf16 fragment reads within a tile. The
+// swizzle only permutes 16-byte chunks inside a 128-byte row and depends on
+// row bits 1..3, so the unit (32 rows) and the 16-key step (16 rows) enter as
+// plain byte offsets; what differs per lane is kept here, once per wave:
+//   k[st]     K operand, k-step st (chunk 2*st + g of row kperm16(lane%32))
+//   v[w][dh]  transposed V read w (rows +0 / +4) of d half dh
+struct LdsLanes { int k[4]; int v[2][2]; };
+
+DEV void lds_lanes_init(LdsLanes& ll, int lane) {
+  const int g = lane >> 5;
+  const int row = kperm16(lane & 31);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) ll.k[st] = ElemTraits<__bf16>::lds_off(row, 2 * st + g);
+  const int i16 = lane & 15;
+#pragma unroll
+  for (int w = 0; w < 2; ++w)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      const int col = 32 * dh + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+      const int row0 = 8 * g + (i16 >> 2) + 4 * w;
+      ll.v[w][dh] = ElemTraits<__bf16>::lds_off(row0, col >> 3) + ((col & 7) << 1);
+    }
+}
+
+DEV KFrag load_kfrag(const char* kbuf, int kh, const LdsLanes& ll) {
+  KFrag k;
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    k.v[st] = *reinterpret_cast<const bf16x8*>(kbuf + 32 * kh * ElemTraits<__bf16>::ROWB + ll.k[st]);
+  return k;
+}
+
+DEV f32x16 score_from(const KFrag& k, const QFrag<__bf16>& qf) {
+  f32x16 s = {};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) s = mfma_bf16(k.v[st], qf.v[st], s);
+  return s;
+}
+
+DEV VFrag load_vfrag(const char* vbuf, int kh, const LdsLanes& ll) {
+  VFrag v;
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) {
+      const char* b = vbuf + (32 * kh + 16 * sp) * ElemTraits<__bf16>::ROWB;
+      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + ll.v[0][dh]));
+      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + ll.v[1][dh]));
+      v.a[sp][dh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  return v;
+}
+
+// Online-softmax update for one unit (bf16): returns the bf16 P operand.
+DEV PFrag softmax_p(WaveAcc& acc, const f32x16& s, float c2) {
+  float mx = s[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[j]);
+  if (__builtin_amdgcn_ballot_w64(mx > acc.thr)) {
+    const float pm = pair_max(mx);
+    const bool upd = pm > acc.thr;
+    const float alpha = upd ? __builtin_amdgcn_exp2f((acc.m - pm) * c2) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc.o[0][i] *= alpha; acc.o[1][i] *= alpha; }
+    acc.l *= alpha;
+    acc.m = upd ? pm : acc.m;
+    acc.thr = acc.m + RESCALE_LOG2 / c2;
+    acc.moff = acc.m == -__builtin_inff() ? 0.f : -acc.m * c2;
+  }
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  PFrag pf;
+  float l = acc.l;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
+    const bf16x2 t = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+    l = __builtin_amdgcn_fdot2_f32_bf16(t, one, l, false);
+    pf.b[j >> 3][j & 7] = t[0];
+    pf.b[j >> 3][(j & 7) + 1] = t[1];
+  }
+  acc.l = l;
+  return pf;
+}
+
+DEV void pv_from(WaveAcc& acc, const VFrag& v, const PFrag& pf) {
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) acc.o[dh] = mfma_bf16(v.a[sp][dh], pf.b[sp], acc.o[dh]);
+}
+
 // Mask one 32-key unit of a band tile: key kk = k0 + key_of_reg(j, g) is
 // allowed for query qi iff qi - half <= kk <= min(qi + right, nr - 1).
 template <class T>
 DEV void mask_band_unit(f32x16& s, int k0, int qi, int half, int right, int nr, int g) {
-  const int lo = qi - half - k0;
-  const int hi = min(qi + right, nr - 1) - k0;
+  const int lo = qi - half - k0 - g * key_g_step<T>;
+  const int hi = min(qi + right, nr - 1) - k0 - g * key_g_step<T>;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int off = key_of_reg<T>(j, g);
+    const int off = key_reg_base<T>(j);
     if (off < lo || off > hi) s[j] = -__builtin_inff();
   }
 }
@@ -518,6 +632,7 @@ struct RingCtx {
   int wave, lane, g;
   bool live;            // this wave has query rows to compute
   float c2;
+  LdsLanes ll;          // lane offsets of the bf16 fragment reads
 };
 
 // Which 32-key units a band wave computes and how they are masked: row qi
@@ -540,11 +655,10 @@ struct GlobPol {
   DEV bool active(int ku) const { return ku < k_hi; }
   DEV bool interior(int ku) const { return ku + 31 < k_hi && (!causal || ku + 31 <= gmin); }
   template <class T> DEV void mask(f32x16& s, int ku, int g) const {
+    const int top = min(k_hi - 1, lim) - ku - g * key_g_step<T>;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kk = ku + key_of_reg<T>(j, g);
-      if (kk >= k_hi || kk > lim) s[j] = -__builtin_inff();
-    }
+    for (int j = 0; j < 16; ++j)
+      if (key_reg_base<T>(j) > top) s[j] = -__builtin_inff();
   }
 };
 
@@ -574,9 +688,16 @@ DEV void ring_step(int tb, WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, c
   for (int kh = 0; kh < 2; ++kh) {
     const int ku = k0 + 32 * kh;
     if (!pol.active(ku)) continue;  // wave-uniform skip
-    f32x16 sc = score_unit(cur, kh, qf, c.lane);
-    if (!pol.interior(ku)) pol.template mask<T>(sc, ku, c.g);
-    softmax_pv_unit<T>(acc, sc, cur + TILEB, kh, c.lane, c.c2);
+    if constexpr (sizeof(T) == 2) {
+      f32x16 sc = score_from(load_kfrag(cur, kh, c.ll), qf);
+      const VFrag v = load_vfrag(cur + TILEB, kh, c.ll);  // in flight during the softmax
+      if (!pol.interior(ku)) pol.template mask<T>(sc, ku, c.g);
+      pv_from(acc, v, softmax_p(acc, sc, c.c2));
+    } else {
+      f32x16 sc = score_unit(cur, kh, qf, c.lane);
+      if (!pol.interior(ku)) pol.template mask<T>(sc, ku, c.g);
+      softmax_pv_unit<T>(acc, sc, cur + TILEB, kh, c.lane, c.c2);
+    }
   }
 }
 
@@ -615,20 +736,119 @@ DEV void ring_run(WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, const Pol&
 // Band block: 128 query rows of one residue class, with the global columns
 // folded in as extra key tiles.
 
+typedef __attribute__((address_space(4))) const TileRec const_TileRec;
+
+DEV TileRec decode_tile(const BandParams& p, int tile) {
+  // the list is read-only for the whole launch: a scalar load
+  TileRec t;
+  if (p.tiles) {
+    const_TileRec* x = (const_TileRec*)p.tiles + tile;
+    t.bh = x->bh; t.r = x->r; t.q0 = x->q0; t.nr = x->nr;
+    t.half = x->half; t.right = x->right; t.dil = x->dil; t.pad = 0;
+    return t;
+  }
+  const int per_bh = p.uni_dil * p.uni_nqb;
+  t.bh = tile / per_bh;
+  const int rem = tile - t.bh * per_bh;
+  t.r = rem / p.uni_nqb;
+  t.q0 = (rem - t.r * p.uni_nqb) * BM;
+  t.nr = (p.n - t.r + p.uni_dil - 1) / p.uni_dil;
+  t.half = p.uni_half;
+  t.right = p.uni_right;
+  t.dil = p.uni_dil;
+  t.pad = 0;
+  return t;
+}
+
+// Global-column keys: the rows of the gather of keys t0 .. t0+63 that this
+// lane's four load instructions fetch (clamped to the last global token).
+DEV void gather_rows(int (&gq)[4], const int* gidx, int t0, int ng, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = 4 * (wave & 1) + i;
+    gq[i] = gidx[min(t0 + blk * Dma<__bf16>::RPI + lane / Dma<__bf16>::CPR, ng - 1)];
+  }
+}
+
+// Direct global->LDS gather of K and V rows gq (absolute positions) into
+// `stage`, laid out as a ring tile.
+DEV void dma_gather(unsigned stage, const char* kb, const char* vb, const int (&gq)[4], int wave,
+                    int lane) {
+  using D = Dma<__bf16>;
+  static_assert(D::PER_WAVE == 4, "four gather instructions per wave");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int I = wave * 4 + i;
+    const int tensor = I / (D::NI / 2);
+    const int blk = I % (D::NI / 2);
+    const int row = blk * D::RPI + lane / D::CPR;
+    const char* src = (tensor ? vb : kb) + (long)gq[i] * D::ROWB +
+                      (ElemTraits<__bf16>::phys(row, lane % D::CPR) << 4);
+    dma16(src, stage + (unsigned)(tensor * (KT * D::ROWB) + blk * 1024));
+  }
+}
+
+// Key metadata of a global-column tile: absolute position (or a value past
+// every limit for padding) and residue-local index (or a sentinel when the
+// key is not in this residue class).
+DEV void gmeta_write(int (*gmeta)[KT], int kpos, bool real, int r, int dil, int tid) {
+  int kp = 0x7fffffff, kr = NEG_SENTINEL;
+  if (real) {
+    kp = kpos;
+    const int dr = kp - r;
+    if (dr >= 0 && dr % dil == 0) kr = dr / dil;
+  }
+  gmeta[0][tid] = kp;
+  gmeta[1][tid] = kr;
+}
+
+// The global-column units of one gathered tile (keys t0 ..): a key counts for
+// row qi if it is left of the row when causal and not already in its band.
+template <class T>
+DEV void glob_cols_tile(WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, const char* stage,
+                        const int (*gmeta)[KT], int t0, int ng, int qi, int half, int right, int lim) {
+  constexpr int TILEB = KT * ElemTraits<T>::ROWB;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    if (t0 + 32 * kh >= ng) continue;
+    f32x16 s;
+    if constexpr (sizeof(T) == 2) s = score_from(load_kfrag(stage, kh, c.ll), qf);
+    else s = score_unit(stage, kh, qf, c.lane);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kk = 32 * kh + key_of_reg<T>(j, c.g);
+      const int kp = gmeta[0][kk], kr = gmeta[1][kk];
+      const bool inband = kr >= qi - half && kr <= qi + right;
+      if (!(kp <= lim) || inband) s[j] = -__builtin_inff();
+    }
+    if constexpr (sizeof(T) == 2) pv_from(acc, load_vfrag(stage + TILEB, kh, c.ll), softmax_p(acc, s, c.c2));
+    else softmax_pv_unit<T>(acc, s, stage + TILEB, kh, c.lane, c.c2);
+  }
+}
+
 template <class T>
 DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* st2, int (*gmeta)[KT]) {
   constexpr int ROWB = ElemTraits<T>::ROWB;
   constexpr int CPR = ElemTraits<T>::CPR;
   constexpr int TILEB = KT * ROWB;
+  constexpr bool BF16 = sizeof(T) == 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int4 td = p.tiles[tile];
-  const int bh = td.x, r = td.y, q0 = td.z;
-  const HeadInfo hi = p.heads[bh % p.H];
-  const int half = hi.half, right = hi.right, dil = hi.dil;
-  const int nr = (p.n - r + dil - 1) / dil;
+
+  // The indices of the first global-column tile do not depend on the tile
+  // record: their loads go out right behind its scalar load.
+  const TileRec td = decode_tile(p, tile);
+  int gq[4] = {0, 0, 0, 0};
+  int gm = 0;
+  if (BF16 && p.ng > 0) {
+    gather_rows(gq, p.gidx, 0, p.ng, wave, lane);
+    gm = p.gidx[min(lane, p.ng - 1)];
+  }
+  const int bh = td.bh, r = td.r, q0 = td.q0, nr = td.nr;
+  if (q0 >= nr) return;  // an empty residue block (uniform decode only)
+  const int half = td.half, right = td.right, dil = td.dil;
   const long base = (long)bh * p.n * ROWB;
   const char* kb = reinterpret_cast<const char*>(p.k) + base;
   const char* vb = reinterpret_cast<const char*>(p.v) + base;
@@ -645,79 +865,76 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
   const int pos_q = r + min(qi, nr - 1) * dil;
   const int wk_lo = max(0, qw0 - half);
   const int wk_hi = min(nr - 1, qw0 + 31 + right);
+  const int lim = p.causal ? pos_q : 0x7fffffff - 1;
 
-  const RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
-                  (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
-                  wave, lane, g, wave_live, p.c2};
+  RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+            (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
+            wave, lane, g, wave_live, p.c2, {}};
+  lds_lanes_init(c.ll, lane);
   const BandPol pol{qi, qw0, half, right, nr, wk_lo, wk_hi};
   const T* qrow = reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.q) + base + (long)pos_q * ROWB);
   QFrag<T> qf;
   WaveAcc acc;
   acc_init(acc);
-  if (p.ng == 0) {
-    // start the first band tiles, then Q; one wait covers all of them (the
-    // compiler must not see Q in flight inside the ring, where it does not
-    // know about the tile loads)
+
+  if constexpr (BF16) {
+    // One round trip for everything the block starts with: the first
+    // global-column tile into stage 2, band tiles 0 and 1 into stages 0 and
+    // 1, and Q. (The gather goes first: the compiler waits for the indices
+    // it needs with a count that only knows its own loads.)
+    if (p.ng > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
     ring_start<T>(c);
     load_q(qf, qrow, g);
-    wait_vmcnt<0>();
+    if (p.ng > 0) {
+      if (tid < KT) gmeta_write(gmeta, gm, tid < p.ng, r, dil, tid);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (wave_live) glob_cols_tile<T>(acc, qf, c, st2, gmeta, 0, p.ng, qi, half, right, lim);
+      for (int t0 = KT; t0 < p.ng; t0 += KT) {  // more than 64 global tokens
+        gather_rows(gq, p.gidx, t0, p.ng, wave, lane);
+        gm = p.gidx[min(t0 + lane, p.ng - 1)];
+        __syncthreads();  // stage 2 and gmeta are free again
+        dma_gather(c.a2, kb, vb, gq, wave, lane);
+        if (tid < KT) gmeta_write(gmeta, gm, t0 + tid < p.ng, r, dil, tid);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (wave_live) glob_cols_tile<T>(acc, qf, c, st2, gmeta, t0, p.ng, qi, half, right, lim);
+      }
+      // the first ring step's barrier orders these reads of stage 2 before
+      // the load of band tile 2 into it
+    } else {
+      wait_vmcnt<0>();
+    }
   } else {
+    // fp32: two ring stages; the global columns go through stage 0 first
     load_q(qf, qrow, g);
     wait_vmcnt<0>();
-  }
-
-  // (1) global columns: tiles of up to 64 keys gathered from K[G], V[G] into
-  // stage 0. A key is used by a row only if it is left of the row (when
-  // causal) and not already inside the row's band.
-  if (p.ng > 0) {
-    constexpr int NC = TileRegs<T, 256>::NC;
-    const int lim = p.causal ? pos_q : 0x7fffffff - 1;
-    for (int t0 = 0; t0 < p.ng; t0 += KT) {
-      TileRegs<T, 256> tr;
-      int gp[NC];
+    if (p.ng > 0) {
+      constexpr int NC = TileRegs<T, 256>::NC;
+      for (int t0 = 0; t0 < p.ng; t0 += KT) {
+        TileRegs<T, 256> tr;
+        int gp[NC];
 #pragma unroll
-      for (int u = 0; u < NC; ++u) gp[u] = p.gidx[min(t0 + (tid + 256 * u) / CPR, p.ng - 1)];
+        for (int u = 0; u < NC; ++u) gp[u] = p.gidx[min(t0 + (tid + 256 * u) / CPR, p.ng - 1)];
 #pragma unroll
-      for (int u = 0; u < NC; ++u) {
-        const long off = (long)gp[u] * ROWB + ((tid + 256 * u) % CPR) * 16;
-        tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
-        tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
-      }
-      if (tid < KT) {
-        int kp = 0x7fffffff, kr = NEG_SENTINEL;
-        if (t0 + tid < p.ng) {
-          kp = p.gidx[t0 + tid];
-          const int dr = kp - r;
-          if (dr >= 0 && dr % dil == 0) kr = dr / dil;
+        for (int u = 0; u < NC; ++u) {
+          const long off = (long)gp[u] * ROWB + ((tid + 256 * u) % CPR) * 16;
+          tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
+          tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
         }
-        gmeta[0][tid] = kp;
-        gmeta[1][tid] = kr;
+        if (tid < KT) gmeta_write(gmeta, p.gidx[min(t0 + tid, p.ng - 1)], t0 + tid < p.ng, r, dil, tid);
+        tile_commit<T, 256>(tr, st0, st0 + TILEB, tid);
+        __syncthreads();
+        if (wave_live) glob_cols_tile<T>(acc, qf, c, st0, gmeta, t0, p.ng, qi, half, right, lim);
+        __syncthreads();
       }
-      tile_commit<T, 256>(tr, st0, st0 + TILEB, tid);
-      __syncthreads();
-      if (wave_live) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          if (t0 + 32 * kh >= p.ng) continue;
-          f32x16 s = score_unit(st0, kh, qf, lane);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kk = 32 * kh + key_of_reg<T>(j, g);
-            const int kp = gmeta[0][kk], kr = gmeta[1][kk];
-            const bool inband = kr >= qi - half && kr <= qi + right;
-            if (!(kp <= lim) || inband) s[j] = -__builtin_inff();
-          }
-          softmax_pv_unit<T>(acc, s, st0 + TILEB, kh, lane, p.c2);
-        }
-      }
-      __syncthreads();
     }
-    ring_start<T>(c);  // the prologue has drained every load; start the ring now
+    ring_start<T>(c);
   }
 
-  // (2) band tiles through the ring: the loads of the next tiles are in
-  // flight while tile t is computed. Rows past the band end are clamped to a
-  // valid row; their scores are masked, so their values only ever meet p = 0.
+  // band tiles through the ring: the loads of the next tiles are in flight
+  // while tile t is computed. Rows past the band end are clamped to a valid
+  // row; their scores are masked, so their values only ever meet p = 0.
   ring_run<T>(acc, qf, c, pol, st0, st1, st2);
 
   if (wave_live) {
@@ -761,10 +978,11 @@ DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char*
   if (p.causal) k_hi = min(k_hi, gmax + 1);
   const int nband = k_hi > k_lo ? (k_hi - k_lo + KT - 1) / KT : 0;  // workgroup-uniform
 
-  const RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
-                  (unsigned)(uintptr_t)(lds_void*)st2,
-                  reinterpret_cast<const char*>(p.kg) + base, reinterpret_cast<const char*>(p.vg) + base,
-                  k_lo, k_hi, nband, 0, 1, wave, lane, g, live, p.c2};
+  RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+            (unsigned)(uintptr_t)(lds_void*)st2,
+            reinterpret_cast<const char*>(p.kg) + base, reinterpret_cast<const char*>(p.vg) + base,
+            k_lo, k_hi, nband, 0, 1, wave, lane, g, live, p.c2, {}};
+  lds_lanes_init(c.ll, lane);
   const GlobPol pol{p.causal ? pos_q : 0x7fffffff - 1, k_hi, gmin, p.causal};
   QFrag<T> qf;
   WaveAcc acc;
@@ -799,14 +1017,13 @@ DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char*
 }
 
 // ----------------------------------------------------------------------------
-// The forward kernel: blocks [0, nglob_blocks) are global-row blocks (padded
-// to a multiple of 8 so that the XCD order of the band blocks is unchanged),
-// the rest band blocks. Listing the memory-bound global-row blocks first lets
-// them stream Kg/Vg while the compute-bound band blocks run beside them.
+// The forward kernel: blocks [0, nband_blocks) are band blocks, the rest
+// global-row blocks. The band blocks come first so that all of them start in
+// the first wave of workgroups; the short global-row blocks fill the
+// workgroup slots that band blocks at the sequence ends free early.
 
 template <class T>
-__global__ __launch_bounds__(256) void attn_fwd(BandParams bp, GlobalParams gp, int nglob_blocks,
-                                                int nglob_real) {
+__global__ __launch_bounds__(256, 3) void attn_fwd(BandParams bp, GlobalParams gp, int nband_blocks) {
   constexpr int STAGEB = 2 * KT * ElemTraits<T>::ROWB;
   constexpr int NS = RingCfg<T>::NS;
   __shared__ __attribute__((aligned(1024))) char st0[STAGEB];
@@ -814,11 +1031,8 @@ __global__ __launch_bounds__(256) void attn_fwd(BandParams bp, GlobalParams gp, 
   __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGEB : 1024];
   __shared__ int gmeta[2][KT];  // global-column tile: key position, residue-local index
   const int b = blockIdx.x;
-  if (b < nglob_blocks) {
-    if (b < nglob_real) global_block<T>(gp, b, st0, st1, st2);
-  } else {
-    band_block<T>(bp, xcd_remap(b - nglob_blocks, gridDim.x - nglob_blocks), st0, st1, st2, gmeta);
-  }
+  if (b < nband_blocks) band_block<T>(bp, xcd_remap(b, nband_blocks), st0, st1, st2, gmeta);
+  else global_block<T>(gp, b - nband_blocks, st0, st1, st2);
 }
 
 constexpr int MAX_SPLIT = 256;

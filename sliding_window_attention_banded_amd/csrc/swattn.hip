@@ -1,6 +1,6 @@
 // Host side of the C ABI declared in include/swattn.h: validation, plan
-// construction (per-head table, residue-class tile schedule, sorted global
-// index list, global-row workspace) and the stream-ordered launches.
+// construction (residue-class tile schedule with per-head geometry, sorted
+// global index list, global-row workspace) and the stream-ordered launches.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -42,11 +42,11 @@ void choose_split(int n, int* nsplit, int* ksplit) {
 
 struct swattn_plan {
   int B, H, n, d, causal, ng, dtype, device;
-  int ntiles;
-  int nsplit, ksplit, nqb, ngroup, nglob_blocks, nglob_real;
+  int nband_blocks;       // band workgroups (explicit tiles, or the uniform decode)
+  int uni_half, uni_right, uni_dil, uni_nqb;  // every head alike: no tile list
+  int nsplit, ksplit, nqb, ngroup, nglob_blocks;
   void* dev_mem;          // one allocation, carved below
-  HeadInfo* heads;        // [H]
-  int4* tiles;            // [ntiles]
+  TileRec* tiles;         // [nband_blocks], NULL with the uniform decode
   int* gidx;              // [ng]
   float* part_o;          // [B*H][ng][nsplit][64]
   float* part_ml;         // [B*H][ng][nsplit][2]
@@ -100,66 +100,76 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   // The merge grid has |G| * B*H <= B*H*n <= 2^31 blocks; the forward grid
   // is checked below.
 
-  // per-head table; a window or dilation beyond n behaves as if clipped to n
-  std::vector<HeadInfo> heads(p->heads);
+  // per-head geometry; a window or dilation beyond n behaves as if clipped to n
+  std::vector<int> half(p->heads), dil(p->heads);
+  bool uniform = true;
   for (int h = 0; h < p->heads; ++h) {
-    const int half = std::min(p->window[h] / 2, p->n);
-    const int dil = std::min(p->dilation[h], p->n);
-    heads[h] = HeadInfo{half, p->causal ? 0 : half, dil, 0};
+    half[h] = std::min(p->window[h] / 2, p->n);
+    dil[h] = std::min(p->dilation[h], p->n);
+    uniform = uniform && half[h] == half[0] && dil[h] == dil[0];
   }
-  // tile schedule: (b, h, residue r, 128-row block), neighbours adjacent
-  std::vector<int4> tiles;
-  for (int b = 0; b < p->batch; ++b)
-    for (int h = 0; h < p->heads; ++h) {
-      const int dil = heads[h].dil;
-      for (int r = 0; r < dil; ++r) {
-        const int nr = (p->n - r + dil - 1) / dil;
-        for (int q0 = 0; q0 < nr; q0 += BM) tiles.push_back(make_int4(b * p->heads + h, r, q0, 0));
-      }
-    }
-  if (tiles.size() > (size_t)0x7fffffff) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
+  // tile schedule: (b, h, residue r, 128-row block), neighbours adjacent.
+  // With one geometry for all heads the kernel decodes the block index
+  // itself (residue classes share one block count; a block past the end of
+  // a shorter class does nothing).
+  std::vector<TileRec> tiles;
+  long nband_blocks = 0;
+  if (uniform) {
+    const long nqb = ((p->n + dil[0] - 1) / dil[0] + BM - 1) / BM;
+    nband_blocks = bh * dil[0] * nqb;
+  } else {
+    for (int b = 0; b < p->batch; ++b)
+      for (int h = 0; h < p->heads; ++h)
+        for (int r = 0; r < dil[h]; ++r) {
+          const int nr = (p->n - r + dil[h] - 1) / dil[h];
+          for (int q0 = 0; q0 < nr; q0 += BM)
+            tiles.push_back(TileRec{b * p->heads + h, r, q0, nr, half[h], p->causal ? 0 : half[h], dil[h], 0});
+        }
+    nband_blocks = (long)tiles.size();
+  }
+  if (nband_blocks > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
 
   swattn_plan* pl = new (std::nothrow) swattn_plan();
   if (!pl) return fail(SWATTN_ERR_HIP, "host allocation failed");
   pl->B = p->batch; pl->H = p->heads; pl->n = p->n; pl->d = p->d;
   pl->causal = p->causal; pl->ng = p->n_global; pl->dtype = p->dtype;
-  pl->ntiles = (int)tiles.size();
+  pl->nband_blocks = (int)nband_blocks;
+  pl->uni_half = half[0];
+  pl->uni_right = p->causal ? 0 : half[0];
+  pl->uni_dil = dil[0];
+  pl->uni_nqb = ((p->n + dil[0] - 1) / dil[0] + BM - 1) / BM;
   pl->nqb = (pl->ng + 31) / 32;
   pl->ngroup = (pl->nqb + BAND_WAVES - 1) / BAND_WAVES;
   pl->nsplit = pl->ksplit = 0;
-  pl->nglob_real = pl->nglob_blocks = 0;
+  pl->nglob_blocks = 0;
   if (pl->ng > 0) {
     choose_split(p->n, &pl->nsplit, &pl->ksplit);
-    const long real = (long)pl->nsplit * pl->ngroup * bh;
-    const long padded = (real + 7) / 8 * 8;
-    if (padded + (long)tiles.size() > 0x7fffffffL) {
+    const long nglob = (long)pl->nsplit * pl->ngroup * bh;
+    if (nglob + nband_blocks > 0x7fffffffL) {
       delete pl;
       return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
     }
-    pl->nglob_real = (int)real;
-    pl->nglob_blocks = (int)padded;
+    pl->nglob_blocks = (int)nglob;
   }
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
 
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t sz_heads = al(sizeof(HeadInfo) * heads.size());
-  const size_t sz_tiles = al(sizeof(int4) * tiles.size());
+  const size_t sz_tiles = al(sizeof(TileRec) * std::max<size_t>(tiles.size(), 1));
   const size_t sz_g = al(sizeof(int) * std::max<size_t>(G.size(), 1));
   const size_t nslot = (size_t)bh * pl->ng * pl->nsplit;
   const size_t sz_po = al(sizeof(float) * HD * nslot);
   const size_t sz_pml = al(sizeof(float) * 2 * nslot);
-  const size_t total = sz_heads + sz_tiles + sz_g + sz_po + sz_pml;
+  const size_t total = sz_tiles + sz_g + sz_po + sz_pml;
   e = hipMalloc(&pl->dev_mem, total);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
   char* m = static_cast<char*>(pl->dev_mem);
-  pl->heads = reinterpret_cast<HeadInfo*>(m); m += sz_heads;
-  pl->tiles = reinterpret_cast<int4*>(m); m += sz_tiles;
+  pl->tiles = tiles.empty() ? nullptr : reinterpret_cast<TileRec*>(m); m += sz_tiles;
   pl->gidx = reinterpret_cast<int*>(m); m += sz_g;
   pl->part_o = reinterpret_cast<float*>(m); m += sz_po;
   pl->part_ml = reinterpret_cast<float*>(m);
-  e = hipMemcpy(pl->heads, heads.data(), sizeof(HeadInfo) * heads.size(), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(int4) * tiles.size(), hipMemcpyHostToDevice);
+  e = hipSuccess;
+  if (!tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(pl->dev_mem);
@@ -240,7 +250,9 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   const float scale = 0.125f;  // 1/sqrt(64)
   BandParams bp;
   bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.lse = lse;
-  bp.tiles = pl->tiles; bp.heads = pl->heads; bp.gidx = pl->gidx; bp.ng = pl->ng;
+  bp.tiles = pl->tiles; bp.gidx = pl->gidx; bp.ng = pl->ng;
+  bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
+  bp.uni_nqb = pl->uni_nqb;
   bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   GlobalParams gp;
@@ -255,8 +267,8 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   if (timed) pl->ntimed++;
   hipError_t e = hipSuccess;
   if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  hipLaunchKernelGGL(attn_fwd<T>, dim3(pl->nglob_blocks + pl->ntiles), dim3(256), 0, st, bp, gp,
-                     pl->nglob_blocks, pl->nglob_real);
+  hipLaunchKernelGGL(attn_fwd<T>, dim3(pl->nband_blocks + pl->nglob_blocks), dim3(256), 0, st, bp, gp,
+                     pl->nband_blocks);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch attn_fwd");
   if (timed && (e = hipEventRecord(ev[1], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
