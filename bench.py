@@ -175,22 +175,35 @@ def main():
     # the forward kernel computes the band, the global columns and the global
     # rows' partials; the merge kernel after it only combines partials
     band_kernel_flops = useful_flops(wl)
+    band_kernel_bytes = algorithmic_bytes(wl)
     tokens = wl.batch * wl.n
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     roof = None
     if band_ms:
-        achieved = band_kernel_flops / (band_ms * 1e-3) / 1e12
+        # the roofline that bounds the kernel is the one with the longer floor
+        # at the chip's peaks: algorithmic bytes / HBM peak vs flops / MFMA peak
+        sec = band_ms * 1e-3
+        tflops = band_kernel_flops / sec / 1e12
+        gbs = band_kernel_bytes / sec / 1e9
+        hbm_floor = band_kernel_bytes / (PEAK_HBM_GBS * 1e9)
+        mfma_floor = band_kernel_flops / (peak * 1e12)
         tr = measured_traffic(wl.name)
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak,
-                "traffic": tr,
-                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
-                "kernel": "attn_fwd", "kernel_us": band_ms * 1e3,
-                "algorithmic_gflop_per_launch": band_kernel_flops / 1e9,
-                "algorithmic_gbytes_per_launch": algorithmic_bytes(wl) / 1e9,
-                "hbm_frac_algorithmic": (algorithmic_bytes(wl) / (band_ms * 1e-3) / 1e9)
-                                        / PEAK_HBM_GBS,
-                "merge_us": glob_ms * 1e3 if glob_ms else 0.0}
+        if hbm_floor >= mfma_floor:
+            roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": gbs / PEAK_HBM_GBS}
+        else:
+            roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                    "frac": tflops / peak}
+        roof.update({
+            "traffic": tr,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel": "attn_fwd", "kernel_us": band_ms * 1e3,
+            "algorithmic_bytes_per_launch": band_kernel_bytes,
+            "algorithmic_gflop_per_launch": band_kernel_flops / 1e9,
+            "hbm_floor_us": hbm_floor * 1e6, "mfma_floor_us": mfma_floor * 1e6,
+            "mfma_tflops": tflops, "mfma_frac": tflops / peak,
+            "hbm_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+            "merge_us": glob_ms * 1e3 if glob_ms else 0.0})
 
     line = {
         "metric": METRIC,

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/swattn.h: validation, plan
 // construction (residue-class tile schedule with per-head geometry, sorted
 // global index list, global-row workspace) and the stream-ordered launches.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -265,20 +266,23 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   const bool timed = !pl->ev.empty() && pl->ntimed < swattn_plan::kMaxTimed;
   hipEvent_t* ev = timed ? &pl->ev[4 * (size_t)pl->ntimed] : nullptr;
   if (timed) pl->ntimed++;
-  hipError_t e = hipSuccess;
-  if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  hipLaunchKernelGGL(attn_fwd<T>, dim3(pl->nband_blocks + pl->nglob_blocks), dim3(256), 0, st, bp, gp,
-                     pl->nband_blocks);
-  e = hipGetLastError();
+  // With timing on, the launches carry start/stop events that the runtime
+  // records at the kernel's own start and end (no event packets in between).
+  const dim3 grid(pl->nband_blocks + pl->nglob_blocks), block(256);
+  if (timed)
+    hipExtLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, ev[0], ev[1], 0, bp, gp, pl->nband_blocks);
+  else
+    hipLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, bp, gp, pl->nband_blocks);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch attn_fwd");
-  if (timed && (e = hipEventRecord(ev[1], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (pl->ng > 0) {
-    if (timed && (e = hipEventRecord(ev[2], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    const int bh = pl->B * pl->H;
-    hipLaunchKernelGGL(global_rows_merge<T>, dim3(pl->ng * bh), dim3(256), 0, st, gp);
+    const dim3 mgrid(pl->ng * pl->B * pl->H);
+    if (timed)
+      hipExtLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, ev[2], ev[3], 0, gp);
+    else
+      hipLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, gp);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch global_rows_merge");
-    if (timed && (e = hipEventRecord(ev[3], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   return SWATTN_OK;
 }

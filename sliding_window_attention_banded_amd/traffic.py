@@ -2,9 +2,10 @@
 
 Two modes:
 
-``run``: the program that rocprofv3 observes. It performs a device copy of
-a known size (the calibration: FETCH_SIZE and WRITE_SIZE of a plain copy
-must read the copy's size) and then a few forwards of one workload::
+``run``: the program that rocprofv3 observes. It runs an elementwise kernel
+over a buffer of known size (the calibration: FETCH_SIZE and WRITE_SIZE of
+a plain streaming kernel must read that size) and then a few forwards of
+one workload::
 
     rocprofv3 --pmc FETCH_SIZE -d OUT_F -o t -- \\
         python -m sliding_window_attention_banded_amd.traffic run --workload W
@@ -52,7 +53,7 @@ def run(workload, reps):
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    dst.copy_(src)  # the calibration copy: COPY_BYTES read, COPY_BYTES written
+    torch.add(src, 1.0, out=dst)  # the calibration kernel: COPY_BYTES read, COPY_BYTES written
     torch.cuda.synchronize()
     wl = WORKLOADS[workload]
     x = {k: (v.to(dev) if v is not None else None) for k, v in make_inputs(wl, 0).items()}
@@ -112,8 +113,15 @@ def summarize(fetch_dir, write_dir, workload, out):
     rec["kernel_sha256_16"] = kernel_source_hash()
     rec["kernel"] = FWD_KERNEL
     rec["method"] = ("rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch); "
-                     "each scaled by COPY_BYTES / (the same counter for a device copy of "
-                     "COPY_BYTES bytes); median over dispatches")
+                     "each scaled by COPY_BYTES / (the same counter for an elementwise kernel "
+                     "that reads and writes COPY_BYTES bytes); median over dispatches")
+    rec["commands"] = [
+        "rocprofv3 --pmc FETCH_SIZE -d OUT_F -o t -- python -m "
+        "sliding_window_attention_banded_amd.traffic run --workload W",
+        "rocprofv3 --pmc WRITE_SIZE -d OUT_W -o t -- python -m "
+        "sliding_window_attention_banded_amd.traffic run --workload W",
+        "python -m sliding_window_attention_banded_amd.traffic summarize OUT_F OUT_W "
+        "--workload W --out profiles/attn_fwd_traffic.json"]
     rec["copy_bytes"] = COPY_BYTES
     rec["workloads"][workload] = {
         "fetch_bytes_per_launch": fv, "write_bytes_per_launch": wv,
