@@ -105,8 +105,10 @@ int swattn_destroy(swattn_plan* plan);
 
 /*
  * Measurement hooks (not part of the computation). With timing enabled, each
- * forward records HIP events on its stream around the band kernel and around
- * the global-row pass (partial + merge); up to 4096 forwards are kept.
+ * forward's two kernels are launched with start/stop HIP events that the
+ * runtime records at the kernel's own start and end on the forward's stream:
+ * the forward kernel (band rows, global columns and the global rows'
+ * partials) and the global-row merge; up to 4096 forwards are kept.
  * swattn_kernel_times() waits for the recorded events, returns the average
  * duration in milliseconds of each phase over the recorded forwards and the
  * number of forwards averaged, then clears the record. Enabling creates the

@@ -21,7 +21,8 @@
 //    merge would.
 //  * global-row blocks: rows of G against a chunk of all keys with Qg, Kg,
 //    Vg, through the same ring; each writes an unnormalised partial (o, m, l)
-//    per chunk. They share one launch (attn_fwd) with the band blocks.
+//    per chunk. They share one launch (attn_fwd) with the band blocks and
+//    come after them in the grid.
 //  * global_rows_merge: log-sum-exp merge of the chunks; overwrites rows G of
 //    O (and LSE), stream-ordered after attn_fwd.
 //
