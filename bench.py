@@ -13,7 +13,6 @@ Cache; the warm (single input set) figure is reported beside it.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,10 +30,6 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "attn_fwd_traffic.json")
 KERNEL_SRC = os.path.join(HERE, "sliding_window_attention_banded_amd", "csrc", "kernels.hpp")
 
 
-def kernel_source_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-
-
 def measured_traffic(workload):
     """HBM bytes per forward-kernel launch from committed rocprofv3 counters,
     or None when absent or taken on a different kernel source."""
@@ -43,7 +38,8 @@ def measured_traffic(workload):
     except (OSError, ValueError):
         return None
     ent = rec.get("workloads", {}).get(workload)
-    if not ent or rec.get("kernel_sha256_16") != kernel_source_hash():
+    from sliding_window_attention_banded_amd.traffic import kernel_source_hash
+    if not ent or rec.get("kernel_sha256_16") != kernel_source_hash(KERNEL_SRC):
         return None
     return ent.get("hbm_bytes_per_launch")
 
