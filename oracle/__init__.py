@@ -18,6 +18,7 @@ force, closed forms, library reductions and hand-derived golden values.
 from .masked_softmax import (  # noqa: F401
     allowed_mask,
     attention,
+    attention_backward,
     band_mask,
     global_row_mask,
 )

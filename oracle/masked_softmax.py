@@ -41,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["band_mask", "global_row_mask", "allowed_mask", "attention"]
+__all__ = ["band_mask", "global_row_mask", "allowed_mask", "attention", "attention_backward"]
 
 
 def band_mask(rows, n, window, dilation, causal):
@@ -168,3 +168,87 @@ def attention(q, k, v, qg=None, kg=None, vg=None, *, window, dilation,
                     o[b, h, s0 + np.nonzero(~reg)[0]] = oo
                     lse[b, h, s0 + np.nonzero(~reg)[0]] = ll
     return o, lse
+
+
+def _masked_softmax_grad_rows(qr, k, v, dor, mask, scale):
+    """Gradients of O = softmax(scale * qr k^T restricted to mask) v for the
+    cotangent ``dor``: returns (dqr, dk, dv) with dk, dv over all n keys.
+
+    The chain rule written out from the definition of the softmax: with P the
+    row-normalised weights, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P
+    * dP)), dQ = scale * dS K, dK = scale * dS^T Q.
+    """
+    s = scale * (qr @ k.T)
+    s = np.where(mask, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    p /= p.sum(axis=1, keepdims=True)
+    dp = dor @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ k), scale * (ds.T @ qr), p.T @ dor
+
+
+def attention_backward(q, k, v, qg, kg, vg, do, *, window, dilation, causal=False,
+                       global_idx=(), row_block=1024):
+    """Oracle backward: gradients of every input for the cotangent ``do`` of O.
+
+    Returns (dq, dk, dv, dqg, dkg, dvg), float64 arrays of q's shape; the
+    global-projection gradients are None when G is empty. A non-global row i
+    depends on q_i and on k_j, v_j for j in A(i); a global row g on qg_g and
+    on kg_j, vg_j for every allowed j (section 3-1, readings R1-R8). Rows of G
+    take their output from the global projections only, so dq is zero there,
+    and dqg is zero off G.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, n, d = q.shape
+    for t in (k, v, do):
+        if t.shape != q.shape:
+            raise ValueError("k, v, do must have q's [B,H,n,d] shape")
+    gl = np.asarray(global_idx, dtype=np.int64).reshape(-1)
+    if gl.size:
+        if len(np.unique(gl)) != gl.size:
+            raise ValueError("global_idx repeats an index")
+        if gl.min() < 0 or gl.max() >= n:
+            raise ValueError("global_idx out of range")
+        qg = np.asarray(qg, dtype=np.float64)
+        kg = np.asarray(kg, dtype=np.float64)
+        vg = np.asarray(vg, dtype=np.float64)
+        for t in (qg, kg, vg):
+            if t.shape != q.shape:
+                raise ValueError("qg, kg, vg must have q's shape")
+    win = np.broadcast_to(np.asarray(window, dtype=np.int64), (H,))
+    dil = np.broadcast_to(np.asarray(dilation, dtype=np.int64), (H,))
+    isg = np.zeros(n, dtype=bool)
+    isg[gl] = True
+    scale = 1.0 / np.sqrt(d)
+
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
+    if gl.size:
+        dqg, dkg, dvg = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
+    else:
+        dqg = dkg = dvg = None
+    rows = np.arange(n)
+    for b in range(B):
+        for h in range(H):
+            for s0 in range(0, n, row_block):
+                rb = rows[s0:s0 + row_block]
+                mask = allowed_mask(rb, n, int(win[h]), int(dil[h]), causal, gl)
+                reg = ~isg[rb]
+                if reg.any():
+                    r = rb[reg]
+                    a, bk, bv = _masked_softmax_grad_rows(q[b, h, r], k[b, h], v[b, h],
+                                                          do[b, h, r], mask[reg], scale)
+                    dq[b, h, r] = a
+                    dk[b, h] += bk
+                    dv[b, h] += bv
+                if (~reg).any():
+                    r = rb[~reg]
+                    a, bk, bv = _masked_softmax_grad_rows(qg[b, h, r], kg[b, h], vg[b, h],
+                                                          do[b, h, r], mask[~reg], scale)
+                    dqg[b, h, r] = a
+                    dkg[b, h] += bk
+                    dvg[b, h] += bv
+    return dq, dk, dv, dqg, dkg, dvg
