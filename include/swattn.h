@@ -98,6 +98,31 @@ int swattn_forward(swattn_plan* plan, const void* q, const void* k,
                    const void* vg, void* o, float* lse, void* stream);
 
 /*
+ * Enqueue the backward pass of one forward on `stream` and return without
+ * waiting: the gradients of Q, K, V (and of Qg, Kg, Vg) for a cotangent dout
+ * of O. With P_ij = exp(s q_i.k_j - LSE_i) on the key set A(i) of the
+ * forward (section 3-1 of the Longformer summary page, as above):
+ *   D_i = dout_i . O_i,  dS_ij = P_ij (dout_i.v_j - D_i),
+ *   dq_i = s sum_j dS_ij k_j,  dk_j = s sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i,
+ * and the same with Qg, Kg, Vg for the rows of G (which take nothing from
+ * Q, K, V: dq is zero on them).
+ *   q .. vg   the forward's inputs (same rules as swattn_forward);
+ *   o, lse    the forward's outputs for those inputs (lse is required);
+ *   dout      device [B, H, n, d] plan dtype;
+ *   dq, dk, dv        device [B, H, n, d] plan dtype, written in full;
+ *   dqg, dkg, dvg     the same for the global projections; NULL exactly
+ *                     when n_global == 0.
+ * Gradients must not overlap each other or any input. The plan's workspace
+ * holds per-row statistics, so a plan runs one backward (or forward) at a
+ * time. bf16 plans only. Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (fp32
+ * plan; n_global > 0 is not implemented yet), HIP.
+ */
+int swattn_backward(swattn_plan* plan, const void* q, const void* k, const void* v,
+                    const void* qg, const void* kg, const void* vg, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* dqg, void* dkg, void* dvg, void* stream);
+
+/*
  * Free the plan and its device memory. NULL is a no-op. The caller must make
  * sure no enqueued forward still uses the plan (e.g. synchronise its stream).
  */

@@ -1,6 +1,6 @@
 """ctypes binding of libswattn.so (argument marshalling only).
 
-Every step of the forward pass runs in the HIP library; this module checks
+Every step of the forward and backward passes runs in the HIP library; this module checks
 tensor shapes and dtypes, hands raw device pointers and the current HIP
 stream to the C ABI, and turns status codes into exceptions. PyTorch is used
 for device memory and streams only. There is no fallback: if the library is
@@ -18,7 +18,7 @@ __all__ = ["Plan", "SwattnError", "library_path", "load_library", "EXPORTS"]
 _HERE = os.path.dirname(os.path.abspath(__file__))
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIGNMENT = range(5)
 BF16, FP32 = 0, 1
-EXPORTS = ("swattn_create", "swattn_forward", "swattn_destroy",
+EXPORTS = ("swattn_create", "swattn_forward", "swattn_backward", "swattn_destroy",
            "swattn_set_timing", "swattn_kernel_times",
            "swattn_status_string", "swattn_last_error")
 
@@ -61,6 +61,8 @@ def load_library():
     lib.swattn_create.restype = ctypes.c_int
     lib.swattn_forward.argtypes = [vp] * 8 + [vp, vp]
     lib.swattn_forward.restype = ctypes.c_int
+    lib.swattn_backward.argtypes = [vp] * 17
+    lib.swattn_backward.restype = ctypes.c_int
     lib.swattn_destroy.argtypes = [vp]
     lib.swattn_destroy.restype = ctypes.c_int
     lib.swattn_set_timing.argtypes = [vp, ctypes.c_int]
@@ -151,6 +153,30 @@ class Plan:
         return out, lse
 
     __call__ = forward
+
+    def backward(self, q, k, v, o, lse, dout, qg=None, kg=None, vg=None,
+                 grads=None, stream=None):
+        """Enqueue the backward pass of a forward with these inputs and
+        outputs (o, lse) for the cotangent ``dout``; returns the gradients
+        (dq, dk, dv, dqg, dkg, dvg), the last three None without G.
+        ``grads`` may supply the six output tensors."""
+        if self._h is None:
+            raise SwattnError(ERR_INVALID_ARG, "plan is closed")
+        if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                or tuple(lse.shape) != (self.batch, self.heads, self.n):
+            raise SwattnError(ERR_INVALID_ARG, "lse must be contiguous fp32 [B, H, n]")
+        has_g = bool(self.global_idx)
+        if grads is None:
+            grads = tuple(torch.empty_like(q) if (i < 3 or has_g) else None for i in range(6))
+        names = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
+        gp = [self._ptr(t, nm) for t, nm in zip(grads, names)]
+        ptrs = [self._ptr(q, "q"), self._ptr(k, "k"), self._ptr(v, "v"),
+                self._ptr(qg, "qg"), self._ptr(kg, "kg"), self._ptr(vg, "vg"),
+                self._ptr(o, "o"), lse.data_ptr(), self._ptr(dout, "dout")] + gp
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        _check(self._lib, self._lib.swattn_backward(self._h, *ptrs, ctypes.c_void_p(st.cuda_stream)),
+               "swattn_backward")
+        return tuple(grads)
 
     def set_timing(self, enable=True):
         """Record HIP events around each kernel phase of later forwards."""

@@ -1,0 +1,441 @@
+// Device kernels of the backward pass (bf16), built from the forward's
+// machinery (kernels.hpp): residue-class tiles, the direct-to-LDS ring, the
+// 32-key unit and its MFMA layouts.
+//
+// For a cotangent dO of O and the forward's LSE, with P_ij = exp(s q_i.k_j -
+// LSE_i) over the row's key set A(i) (Longformer summary page, section 3-1):
+//   D_i   = dO_i . O_i                 (= sum_j P_ij dO_i.v_j)
+//   dS_ij = P_ij (dO_i.v_j - D_i)
+//   dq_i  = s sum_j dS_ij k_j,   dk_j = s sum_i dS_ij q_i,   dv_j = sum_i P_ij dO_i.
+// Rows of G take their output from the global projections only, so the band
+// passes treat them as absent: their log2-LSE is set to +inf (P = 0).
+//
+// Kernels:
+//  * bwd_prep: D_i and the log2-domain LSE (+inf on rows of G), per row.
+//  * bwd_main, band query blocks: 128 query rows of one residue class, Q and
+//    dO in registers, key tiles (K, V) through the ring, the global-column
+//    tile first: dq = s dS K.
+//  * bwd_main, band key blocks: 128 keys of one residue class, K and V in
+//    registers, query tiles (Q, dO, log2-LSE, D) through the ring: dk, dv.
+//
+// Score tiles again come out transposed from the MFMA so that the
+// probabilities (and dS) are already the B operand of the next product:
+//  * query blocks: S^T = K Q^T and dP^T = V dO^T (lane = query), then
+//    dQ^T += K^T dS^T with K^T read transposed from LDS;
+//  * key blocks: T = Q K^T and dP = dO V^T (lane = key; Q, dO rows fed in
+//    the permuted row order), then dV^T += dO^T P and dK^T += Q^T dS with
+//    dO^T, Q^T read transposed from LDS.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace swattn {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // [BH][n], natural log (the forward's output)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* lse2;        // [BH][n]: LSE * log2(e), +inf on rows of G
+  float* dd;          // [BH][n]: D
+  const TileRec* tiles;
+  int uni_half, uni_right, uni_dil, uni_nqb;
+  const int* gidx;
+  int ng;
+  int n;
+  int causal;
+  int nband_blocks;   // query blocks; the key blocks follow, as many
+  float c2;           // scale * log2(e)
+  float scale;
+};
+
+// ----------------------------------------------------------------------------
+// Row statistics: 8 lanes per row, 8 elements each.
+
+__global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = t >> 3;
+  const int part = threadIdx.x & 7;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.o) + row * HD + 8 * part);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.dout) + row * HD + 8 * part);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+  }
+  // sum the 8 lanes of the row (aligned groups of 8 within the wave)
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && part == 0) {
+    const int i = (int)(row % p.n);
+    // G is sorted: binary search for i
+    int lo = 0, hi = p.ng;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.gidx[mid] < i) lo = mid + 1;
+      else hi = mid;
+    }
+    const bool isg = lo < p.ng && p.gidx[lo] == i;
+    p.lse2[row] = isg ? __builtin_inff() : p.lse[row] * LOG2E;
+    p.dd[row] = acc;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Shared pieces.
+
+// One 4-byte-per-lane global->LDS load (lane l lands at lds + 4 l).
+DEV void dma4(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// A pair of fp32 accumulators for a 64-wide row block of 32 lanes (the same
+// layout as the forward's O^T accumulator).
+struct Acc2 { f32x16 a[2]; };
+
+DEV void acc2_zero(Acc2& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { x.a[0][i] = 0.f; x.a[1][i] = 0.f; }
+}
+
+DEV void acc2_mma(Acc2& x, const VFrag& v, const PFrag& pf) {
+#pragma unroll
+  for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh) x.a[dh] = mfma_bf16(v.a[sp][dh], pf.b[sp], x.a[dh]);
+}
+
+// Row of 64 for this lane (lane l and l^32 hold alternate 4-element groups).
+DEV void store_row(__bf16* row, const Acc2& x, float f, int g) {
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(x.a[dh][4 * a + e] * f);
+      *reinterpret_cast<bf16x4*>(row + 32 * dh + 8 * a + 4 * g) = t;
+    }
+}
+
+// Two f32x16 into the bf16 B-operand fragment (register j of the accumulator
+// is element j%8 of step j/8, as for P in the forward).
+DEV PFrag to_bfrag(const f32x16& x) {
+  PFrag pf;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const bf16x2 t = __builtin_convertvector(f32x2{x[j], x[j + 1]}, bf16x2);
+    pf.b[j >> 3][j & 7] = t[0];
+    pf.b[j >> 3][(j & 7) + 1] = t[1];
+  }
+  return pf;
+}
+
+// ----------------------------------------------------------------------------
+// Query blocks: dq.
+
+struct DqWave {
+  QFrag<__bf16> qf, dof;
+  float lse2, dd;
+  Acc2 dq;
+};
+
+// One 32-key unit of a K/V tile in LDS (K at kbuf, V at vbuf); `masked` is
+// applied to the raw scores before the exponential.
+template <class MaskFn>
+DEV void dq_unit(DqWave& w, const char* kbuf, const char* vbuf, int kh, const LdsLanes& ll,
+                 float c2, bool need_mask, MaskFn&& mask) {
+  f32x16 s = score_from(load_kfrag(kbuf, kh, ll), w.qf);
+  const f32x16 dp = score_from(load_kfrag(vbuf, kh, ll), w.dof);
+  const VFrag kt = load_vfrag(kbuf, kh, ll);  // K^T, in flight during the VALU work
+  if (need_mask) mask(s);
+  f32x16 ds;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -w.lse2));
+    ds[j] = pj * (dp[j] - w.dd);
+  }
+  acc2_mma(w.dq, kt, to_bfrag(ds));
+}
+
+// The ring for query blocks (K/V tiles, as in the forward).
+template <int S, class Pol>
+DEV void dq_ring_step(int tb, DqWave& w, const RingCtx& c, const Pol& pol, const DmaLanes<__bf16>& dl,
+                      const char* st0, const char* st1, const char* st2) {
+  constexpr int TILEB = KT * ElemTraits<__bf16>::ROWB;
+  const char* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
+  constexpr int SN = (S + 2) % 3;
+  const unsigned nxt = SN == 0 ? c.a0 : (SN == 1 ? c.a1 : c.a2);
+  wait_vmcnt<Dma<__bf16>::PER_WAVE>();
+  wg_barrier();
+  const int kn = c.kbeg + min(tb + 2, c.nband - 1) * KT;
+  if (kn + KT <= c.kend) dma_tile_fast<__bf16>(nxt, dl, c.kb, c.vb, kn, c.r, c.dil, c.wave);
+  else dma_tile<__bf16>(nxt, c.kb, c.vb, kn, c.kend, c.r, c.dil, c.wave, c.lane);
+  if (!c.live) return;
+  const int k0 = c.kbeg + tb * KT;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int ku = k0 + 32 * kh;
+    if (!pol.active(ku)) continue;
+    dq_unit(w, cur, cur + TILEB, kh, c.ll, c.c2, !pol.interior(ku),
+            [&](f32x16& s) { pol.template mask<__bf16>(s, ku, c.g); });
+  }
+}
+
+DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* st2, int (*gmeta)[KT]) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  constexpr int TILEB = KT * ROWB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  BandParams bp;  // the tile decode reads only these fields
+  bp.tiles = p.tiles; bp.uni_half = p.uni_half; bp.uni_right = p.uni_right;
+  bp.uni_dil = p.uni_dil; bp.uni_nqb = p.uni_nqb; bp.n = p.n;
+  const TileRec td = decode_tile(bp, tile);
+  int gq[4] = {0, 0, 0, 0};
+  int gm = 0;
+  if (p.ng > 0) {
+    gather_rows(gq, p.gidx, 0, p.ng, wave, lane);
+    gm = p.gidx[min(lane, p.ng - 1)];
+  }
+  const int bh = td.bh, r = td.r, q0 = td.q0, nr = td.nr;
+  if (q0 >= nr) return;
+  const int half = td.half, right = td.right, dil = td.dil;
+  const long base = (long)bh * p.n * ROWB;
+  const char* kb = reinterpret_cast<const char*>(p.k) + base;
+  const char* vb = reinterpret_cast<const char*>(p.v) + base;
+  const int kbeg = max(0, q0 - half);
+  const int kend = min(nr, q0 + BM + right);
+  const int nband = (kend - kbeg + KT - 1) / KT;
+  const int qw0 = q0 + 32 * wave;
+  const bool wave_live = qw0 < nr;
+  const int qi = qw0 + (lane & 31);
+  const bool row_ok = qi < nr;
+  const int pos_q = r + min(qi, nr - 1) * dil;
+  const int lim = p.causal ? pos_q : 0x7fffffff - 1;
+
+  RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+            (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
+            wave, lane, g, wave_live, p.c2, {}};
+  lds_lanes_init(c.ll, lane);
+  const BandPol pol{qi, qw0, half, right, nr, max(0, qw0 - half), min(nr - 1, qw0 + 31 + right)};
+
+  DqWave w;
+  acc2_zero(w.dq);
+  const long roff = base + (long)pos_q * ROWB;
+  if (p.ng > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
+  ring_start<__bf16>(c);
+  load_q(w.qf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.q) + roff), g);
+  load_q(w.dof, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.dout) + roff), g);
+  w.lse2 = p.lse2[(long)bh * p.n + pos_q];
+  w.dd = p.dd[(long)bh * p.n + pos_q];
+  if (p.ng > 0) {
+    if (tid < KT) gmeta_write(gmeta, gm, tid < p.ng, r, dil, tid);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int t0 = 0;;) {
+      if (wave_live) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          if (t0 + 32 * kh >= p.ng) continue;
+          dq_unit(w, st2, st2 + TILEB, kh, c.ll, p.c2, true, [&](f32x16& s) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int kk = 32 * kh + key_of_reg<__bf16>(j, g);
+              const int kp = gmeta[0][kk], kr = gmeta[1][kk];
+              const bool inband = kr >= qi - half && kr <= qi + right;
+              if (!(kp <= lim) || inband) s[j] = -__builtin_inff();
+            }
+          });
+        }
+      }
+      t0 += KT;
+      if (t0 >= p.ng) break;
+      gather_rows(gq, p.gidx, t0, p.ng, wave, lane);
+      gm = p.gidx[min(t0 + lane, p.ng - 1)];
+      __syncthreads();
+      dma_gather(c.a2, kb, vb, gq, wave, lane);
+      if (tid < KT) gmeta_write(gmeta, gm, t0 + tid < p.ng, r, dil, tid);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  } else {
+    wait_vmcnt<0>();
+  }
+
+  DmaLanes<__bf16> dl;
+  dma_lanes_init<__bf16>(dl, dil, lane);
+  for (int tb = 0; tb < nband; tb += 3) {
+    dq_ring_step<0>(tb, w, c, pol, dl, st0, st1, st2);
+    if (tb + 1 < nband) dq_ring_step<1>(tb + 1, w, c, pol, dl, st0, st1, st2);
+    if (tb + 2 < nband) dq_ring_step<2>(tb + 2, w, c, pol, dl, st0, st1, st2);
+  }
+  wait_vmcnt<0>();
+
+  if (wave_live && row_ok)
+    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dq) + roff), w.dq, p.scale, g);
+}
+
+// ----------------------------------------------------------------------------
+// Key blocks: dk, dv.
+//
+// A ring stage holds a tile of 64 query rows: Q (8 KB), dO (8 KB) and the
+// rows' log2-LSE and D (256 B each, in the first 512 B of a 1 KB area that
+// the four waves fill: waves 0 and 2 load the log2-LSE, waves 1 and 3 D, the
+// latter pair into a second copy that nobody reads, so that every wave
+// issues the same number of loads).
+
+constexpr int QSTAGEB = 2 * KT * 128 + 1024;
+
+struct DkvWave {
+  QFrag<__bf16> kf, vf;  // this lane's key row of K and of V (B operands)
+  Acc2 dk, dv;
+};
+
+DEV void dma_stats(unsigned stage, const float* lse2, const float* dd, int kb0, int kend, int r,
+                   int dil, int wave, int lane) {
+  const int kk = min(kb0 + lane, kend - 1);
+  const float* src = ((wave & 1) ? dd : lse2) + (r + (long)kk * dil);
+  dma4(src, stage + (unsigned)(2 * KT * 128 + 256 * wave));
+}
+
+// One 32-query unit (rows 32*kh.. of the tile at `stage`).
+template <class MaskFn>
+DEV void dkv_unit(DkvWave& w, const char* stage, int kh, const LdsLanes& ll, float c2, int g,
+                  bool need_mask, MaskFn&& mask) {
+  constexpr int TILEB = KT * 128;
+  f32x16 t = score_from(load_kfrag(stage, kh, ll), w.kf);           // T[q][key]
+  const f32x16 dp = score_from(load_kfrag(stage + TILEB, kh, ll), w.vf);  // dP[q][key]
+  // register j holds query 16*(j/8) + 8g + j%8 of the unit
+  const float* sl = reinterpret_cast<const float*>(stage + 2 * TILEB) + 32 * kh + 8 * g;
+  const float* sd = reinterpret_cast<const float*>(stage + 2 * TILEB + 256) + 32 * kh + 8 * g;
+  const f32x4 l0 = *reinterpret_cast<const f32x4*>(sl), l1 = *reinterpret_cast<const f32x4*>(sl + 4);
+  const f32x4 l2 = *reinterpret_cast<const f32x4*>(sl + 16), l3 = *reinterpret_cast<const f32x4*>(sl + 20);
+  const f32x4 d0 = *reinterpret_cast<const f32x4*>(sd), d1 = *reinterpret_cast<const f32x4*>(sd + 4);
+  const f32x4 d2 = *reinterpret_cast<const f32x4*>(sd + 16), d3 = *reinterpret_cast<const f32x4*>(sd + 20);
+  const VFrag dot = load_vfrag(stage + TILEB, kh, ll);  // dO^T
+  const VFrag qt = load_vfrag(stage, kh, ll);           // Q^T
+  if (need_mask) mask(t);
+  f32x16 pj, ds;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int a = j >> 2, e = j & 3;
+    const float l2j = a == 0 ? l0[e] : a == 1 ? l1[e] : a == 2 ? l2[e] : l3[e];
+    const float ddj = a == 0 ? d0[e] : a == 1 ? d1[e] : a == 2 ? d2[e] : d3[e];
+    pj[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], c2, -l2j));
+    ds[j] = pj[j] * (dp[j] - ddj);
+  }
+  acc2_mma(w.dv, dot, to_bfrag(pj));
+  acc2_mma(w.dk, qt, to_bfrag(ds));
+}
+
+template <int S, class Pol>
+DEV void dkv_ring_step(int tb, DkvWave& w, const RingCtx& c, const Pol& pol, const DmaLanes<__bf16>& dl,
+                       const float* lse2, const float* dd, const char* st0, const char* st1,
+                       const char* st2) {
+  const char* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
+  constexpr int SN = (S + 2) % 3;
+  const unsigned nxt = SN == 0 ? c.a0 : (SN == 1 ? c.a1 : c.a2);
+  wait_vmcnt<Dma<__bf16>::PER_WAVE + 1>();
+  wg_barrier();
+  const int kn = c.kbeg + min(tb + 2, c.nband - 1) * KT;
+  if (kn + KT <= c.kend) dma_tile_fast<__bf16>(nxt, dl, c.kb, c.vb, kn, c.r, c.dil, c.wave);
+  else dma_tile<__bf16>(nxt, c.kb, c.vb, kn, c.kend, c.r, c.dil, c.wave, c.lane);
+  dma_stats(nxt, lse2, dd, kn, c.kend, c.r, c.dil, c.wave, c.lane);
+  if (!c.live) return;
+  const int k0 = c.kbeg + tb * KT;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int ku = k0 + 32 * kh;
+    if (!pol.active(ku)) continue;
+    dkv_unit(w, cur, kh, c.ll, c.c2, c.g, !pol.interior(ku),
+             [&](f32x16& s) { pol.template mask<__bf16>(s, ku, c.g); });
+  }
+}
+
+DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char* st2) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  BandParams bp;
+  bp.tiles = p.tiles; bp.uni_half = p.uni_half; bp.uni_right = p.uni_right;
+  bp.uni_dil = p.uni_dil; bp.uni_nqb = p.uni_nqb; bp.n = p.n;
+  const TileRec td = decode_tile(bp, tile);
+  const int bh = td.bh, r = td.r, k0 = td.q0, nr = td.nr;
+  if (k0 >= nr) return;
+  const int half = td.half, right = td.right, dil = td.dil;
+  const long base = (long)bh * p.n * ROWB;
+  // key j is seen by query i iff i - half <= j <= i + right, i.e. by the
+  // queries j - right .. j + half: the band with its two sides exchanged
+  const int qbeg = max(0, k0 - right);
+  const int qend = min(nr, k0 + BM + half);
+  const int nband = (qend - qbeg + KT - 1) / KT;
+  const int kw0 = k0 + 32 * wave;
+  const bool wave_live = kw0 < nr;
+  const int kj = kw0 + (lane & 31);
+  const bool key_ok = kj < nr;
+  const int pos_k = r + min(kj, nr - 1) * dil;
+
+  RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+            (unsigned)(uintptr_t)(lds_void*)st2,
+            reinterpret_cast<const char*>(p.q) + base, reinterpret_cast<const char*>(p.dout) + base,
+            qbeg, qend, nband, r, dil, wave, lane, g, wave_live, p.c2, {}};
+  lds_lanes_init(c.ll, lane);
+  const BandPol pol{kj, kw0, right, half, nr, max(0, kw0 - right), min(nr - 1, kw0 + 31 + half)};
+  const float* lse2 = p.lse2 + (long)bh * p.n;
+  const float* dd = p.dd + (long)bh * p.n;
+
+  DkvWave w;
+  acc2_zero(w.dk);
+  acc2_zero(w.dv);
+  const long roff = base + (long)pos_k * ROWB;
+  dma_tile<__bf16>(c.a0, c.kb, c.vb, qbeg, qend, r, dil, wave, lane);
+  dma_stats(c.a0, lse2, dd, qbeg, qend, r, dil, wave, lane);
+  const int q1 = qbeg + min(1, nband - 1) * KT;
+  dma_tile<__bf16>(c.a1, c.kb, c.vb, q1, qend, r, dil, wave, lane);
+  dma_stats(c.a1, lse2, dd, q1, qend, r, dil, wave, lane);
+  load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.k) + roff), g);
+  load_q(w.vf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.v) + roff), g);
+  wait_vmcnt<0>();
+
+  DmaLanes<__bf16> dl;
+  dma_lanes_init<__bf16>(dl, dil, lane);
+  for (int tb = 0; tb < nband; tb += 3) {
+    dkv_ring_step<0>(tb, w, c, pol, dl, lse2, dd, st0, st1, st2);
+    if (tb + 1 < nband) dkv_ring_step<1>(tb + 1, w, c, pol, dl, lse2, dd, st0, st1, st2);
+    if (tb + 2 < nband) dkv_ring_step<2>(tb + 2, w, c, pol, dl, lse2, dd, st0, st1, st2);
+  }
+  wait_vmcnt<0>();
+
+  if (wave_live && key_ok) {
+    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dk) + roff), w.dk, p.scale, g);
+    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dv) + roff), w.dv, 1.0f, g);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// The main backward kernel: blocks [0, nband_blocks) are query blocks (dq),
+// blocks [nband_blocks, 2 nband_blocks) key blocks (dk, dv) over the same
+// tile schedule.
+
+__global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char st0[QSTAGEB];
+  __shared__ __attribute__((aligned(1024))) char st1[QSTAGEB];
+  __shared__ __attribute__((aligned(1024))) char st2[QSTAGEB];
+  __shared__ int gmeta[2][KT];
+  const int b = blockIdx.x;
+  if (b < p.nband_blocks) bwd_dq_block(p, xcd_remap(b, p.nband_blocks), st0, st1, st2, gmeta);
+  else bwd_dkv_block(p, xcd_remap(b - p.nband_blocks, p.nband_blocks), st0, st1, st2);
+}
+
+}  // namespace swattn

@@ -13,6 +13,7 @@
 
 #include "swattn.h"
 #include "kernels.hpp"
+#include "backward.hpp"
 
 using namespace swattn;
 
@@ -51,6 +52,8 @@ struct swattn_plan {
   int* gidx;              // [ng]
   float* part_o;          // [B*H][ng][nsplit][64]
   float* part_ml;         // [B*H][ng][nsplit][2]
+  float* bwd_lse2;        // [B*H][n] backward row statistics (bf16 plans)
+  float* bwd_dd;          // [B*H][n]
   // measurement hooks
   static constexpr int kMaxTimed = 4096;
   std::vector<hipEvent_t> ev;  // [kMaxTimed][4]: band start/stop, global start/stop
@@ -128,7 +131,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
         }
     nband_blocks = (long)tiles.size();
   }
-  if (nband_blocks > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
+  // the backward launch holds two blocks per band tile
+  if (2 * nband_blocks > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
 
   swattn_plan* pl = new (std::nothrow) swattn_plan();
   if (!pl) return fail(SWATTN_ERR_HIP, "host allocation failed");
@@ -161,14 +165,17 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const size_t nslot = (size_t)bh * pl->ng * pl->nsplit;
   const size_t sz_po = al(sizeof(float) * HD * nslot);
   const size_t sz_pml = al(sizeof(float) * 2 * nslot);
-  const size_t total = sz_tiles + sz_g + sz_po + sz_pml;
+  const size_t sz_stat = pl->dtype == SWATTN_BF16 ? al(sizeof(float) * (size_t)bh * p->n) : 0;
+  const size_t total = sz_tiles + sz_g + sz_po + sz_pml + 2 * sz_stat;
   e = hipMalloc(&pl->dev_mem, total);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
   char* m = static_cast<char*>(pl->dev_mem);
   pl->tiles = tiles.empty() ? nullptr : reinterpret_cast<TileRec*>(m); m += sz_tiles;
   pl->gidx = reinterpret_cast<int*>(m); m += sz_g;
   pl->part_o = reinterpret_cast<float*>(m); m += sz_po;
-  pl->part_ml = reinterpret_cast<float*>(m);
+  pl->part_ml = reinterpret_cast<float*>(m); m += sz_pml;
+  pl->bwd_lse2 = sz_stat ? reinterpret_cast<float*>(m) : nullptr; m += sz_stat;
+  pl->bwd_dd = sz_stat ? reinterpret_cast<float*>(m) : nullptr;
   e = hipSuccess;
   if (!tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
@@ -315,4 +322,56 @@ extern "C" int swattn_forward(swattn_plan* pl, const void* q, const void* k, con
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (pl->dtype == SWATTN_BF16) return launch<__bf16>(pl, q, k, v, qg, kg, vg, o, lse, st);
   return launch<float>(pl, q, k, v, qg, kg, vg, o, lse, st);
+}
+
+extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, const void* v,
+                               const void* qg, const void* kg, const void* vg, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               void* dqg, void* dkg, void* dvg, void* stream) {
+  g_last_error.clear();
+  if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
+  if (pl->dtype != SWATTN_BF16) return fail(SWATTN_ERR_UNSUPPORTED, "the backward pass is bf16 only");
+  if (pl->ng > 0) return fail(SWATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens yet");
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(SWATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
+  const bool want_g = pl->ng > 0;
+  const void* gs[] = {qg, kg, vg, dqg, dkg, dvg};
+  for (const void* x : gs)
+    if ((x != nullptr) != want_g)
+      return fail(SWATTN_ERR_INVALID_ARG, "qg, kg, vg, dqg, dkg, dvg must be non-NULL exactly when n_global > 0");
+  const void* all[] = {q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv, dqg, dkg, dvg};
+  for (const void* x : all)
+    if (x && !aligned16(x)) return fail(SWATTN_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const size_t nbytes = (size_t)pl->B * pl->H * pl->n * HD * 2;
+  const size_t lb = (size_t)pl->B * pl->H * pl->n * sizeof(float);
+  const void* ins[] = {q, k, v, qg, kg, vg, o, dout};
+  void* outs[] = {dq, dk, dv, dqg, dkg, dvg};
+  for (int a = 0; a < 6; ++a) {
+    if (!outs[a]) continue;
+    for (const void* x : ins)
+      if (overlaps(outs[a], nbytes, x, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "a gradient overlaps an input");
+    if (overlaps(outs[a], nbytes, lse, lb)) return fail(SWATTN_ERR_INVALID_ARG, "a gradient overlaps lse");
+    for (int b = 0; b < a; ++b)
+      if (overlaps(outs[a], nbytes, outs[b], nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "two gradients overlap");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float scale = 0.125f;
+  BwdParams bp;
+  bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.dout = dout; bp.lse = lse;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv;
+  bp.lse2 = pl->bwd_lse2; bp.dd = pl->bwd_dd;
+  bp.tiles = pl->tiles;
+  bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
+  bp.uni_nqb = pl->uni_nqb;
+  bp.gidx = pl->gidx; bp.ng = pl->ng; bp.n = pl->n; bp.causal = pl->causal;
+  bp.nband_blocks = pl->nband_blocks;
+  bp.c2 = scale * LOG2E; bp.scale = scale;
+  const long rows = (long)pl->B * pl->H * pl->n;
+  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st, bp, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch bwd_prep");
+  hipLaunchKernelGGL(bwd_main, dim3(2 * pl->nband_blocks), dim3(256), 0, st, bp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch bwd_main");
+  return SWATTN_OK;
 }

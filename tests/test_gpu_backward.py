@@ -1,0 +1,142 @@
+"""GPU parity of the backward pass: the HIP library's gradients against the
+float64 oracle's, element by element, on the same bf16 inputs and cotangent.
+
+The forward runs on the GPU first (its O and LSE are the backward's inputs,
+as in training); the oracle recomputes everything from the inputs. Small and
+ragged shapes are compared in full; the full-size workloads on whole
+(batch, head) slices, which the oracle computes one at a time.
+
+Tolerance (bf16 gradients, fp32 accumulation): relative RMS <= 1e-2 and
+max-abs <= 2^-5 * max|reference| per tensor. The terms: dS is rounded to
+bf16 before its MFMA (relative 2^-8 per element), D_i is formed from the
+bf16-rounded O (relative 2^-9), P and dP are fp32, and the gradients are
+rounded to bf16 at the end (relative 2^-9 of each element). Summed over a
+row's keys with random signs the first term stays near 2^-8 of the row's
+largest contributions; 2^-5 of the tensor's largest element leaves room for
+rows whose gradient is a cancellation of larger terms. A tensor that
+vanishes exactly (window 0: every row's softmax is a single weight 1, so
+dS = 0 and dq = dk = 0) is held to an absolute 1e-6, the fp32 rounding of
+its O(1) terms.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sliding_window_attention_banded_amd.workloads import WORKLOADS, Workload, make_inputs
+from tests._lib import ensure_library, to64
+
+pytestmark = pytest.mark.gpu
+
+REL, MAXF, FLOOR = 1e-2, 2.0 ** -5, 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+
+
+def W(name, B, H, n, window, dilation, causal=False, G=()):
+    win = (window,) * H if isinstance(window, int) else tuple(window)
+    dil = (dilation,) * H if isinstance(dilation, int) else tuple(dilation)
+    return Workload(name, B, H, n, 64, win, dil, causal, tuple(G), "bf16", 0.125)
+
+
+SMALL = [
+    W("b_uniform", 1, 2, 300, 64, 1),
+    W("b_uniform_causal", 1, 2, 300, 64, 2, True),
+    W("b_mix", 2, 3, 777, (64, 128, 30), (1, 2, 3)),
+    W("b_mix_causal", 1, 4, 500, (32, 256, 2, 1024), (1, 4, 1, 2), True),
+    W("b_short", 1, 2, 40, 16, 1),
+    W("b_one", 1, 1, 1, 8, 1),
+    W("b_wide", 1, 2, 200, (1000, 602), (1, 1)),
+    W("b_window0", 1, 2, 130, (0, 0), (1, 5)),
+]
+
+
+def _cotangent(wl, seed):
+    g = torch.Generator().manual_seed(10_000 + seed)
+    return torch.randn((wl.batch, wl.heads, wl.n, wl.d), generator=g).to(torch.bfloat16)
+
+
+def _gpu_grads(wl, inp, dout):
+    from sliding_window_attention_banded_amd import Plan
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    with Plan(wl.batch, wl.heads, wl.n, wl.d, wl.window, wl.dilation, wl.causal,
+              wl.global_idx, wl.torch_dtype) as pl:
+        o, lse = pl.forward(dev["q"], dev["k"], dev["v"], dev["qg"], dev["kg"], dev["vg"],
+                            want_lse=True)
+        grads = pl.backward(dev["q"], dev["k"], dev["v"], o, lse, dout.cuda(),
+                            dev["qg"], dev["kg"], dev["vg"])
+        torch.cuda.synchronize()
+    return [None if t is None else t.cpu() for t in grads]
+
+
+def _oracle_grads(wl, inp, dout, bh=None):
+    """Oracle gradients, optionally for a list of (b, h) slices only."""
+    from oracle import attention_backward
+    t = [to64(inp[k]) for k in ("q", "k", "v", "qg", "kg", "vg")] + [to64(dout)]
+    win, dil = list(wl.window), list(wl.dilation)
+    if bh is None:
+        return attention_backward(*t, window=win, dilation=dil, causal=wl.causal,
+                                  global_idx=list(wl.global_idx))
+    outs = []
+    for b, h in bh:
+        sl = [None if x is None else x[b:b + 1, h:h + 1] for x in t]
+        outs.append(attention_backward(*sl, window=win[h], dilation=dil[h], causal=wl.causal,
+                                       global_idx=list(wl.global_idx)))
+    return outs
+
+
+def _cmp(got, ref, label):
+    g = got.double().numpy()
+    assert np.isfinite(g).all(), f"{label}: non-finite gradient"
+    err = np.abs(g - ref)
+    scale = max(np.abs(ref).max(), 1e-30)
+    rel = np.sqrt((err ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30)
+    print(f"  {label}: max-abs {err.max():.3e} (max|ref| {scale:.3e}), rel-rms {rel:.3e}", flush=True)
+    assert err.max() <= max(MAXF * scale, FLOOR), f"{label}: max-abs {err.max():.3e} > {MAXF} * {scale:.3e}"
+    if np.sqrt((ref ** 2).mean()) > FLOOR:
+        assert rel <= REL, f"{label}: rel-rms {rel:.3e}"
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("kind", ["normal", "sharp"])
+def test_backward_small(wl, kind):
+    for seed in (0, 1):
+        print(f"[bwd] {wl.name} B{wl.batch} H{wl.heads} n{wl.n} causal={wl.causal} "
+              f"seed={seed} kind={kind}", flush=True)
+        inp = make_inputs(wl, seed, kind)
+        dout = _cotangent(wl, seed)
+        got = _gpu_grads(wl, inp, dout)
+        ref = _oracle_grads(wl, inp, dout)
+        for name, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+            _cmp(a, b, f"{wl.name}/{kind}/{seed}/{name}")
+
+
+@pytest.mark.parametrize("name,bh", [
+    ("encoder_b2_h12_n4096_w512", [(0, 0), (1, 11)]),
+    ("arlm_b1_h12_n8192_w512_causal_dil2", [(0, 3), (0, 11)]),
+])
+@pytest.mark.parametrize("kind", ["normal", "sharp"])
+def test_backward_full_size_slices(name, bh, kind):
+    wl = WORKLOADS[name]
+    print(f"[bwd] {wl.name} slices {bh} kind={kind}", flush=True)
+    inp = make_inputs(wl, 0, kind)
+    dout = _cotangent(wl, 0)
+    got = _gpu_grads(wl, inp, dout)
+    refs = _oracle_grads(wl, inp, dout, bh=bh)
+    for (b, h), ref in zip(bh, refs):
+        for name_g, a, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+            _cmp(a[b:b + 1, h:h + 1], r, f"{wl.name}[{b},{h}]/{kind}/{name_g}")
+
+
+def test_backward_rejects_global_tokens_for_now():
+    from sliding_window_attention_banded_amd import Plan, SwattnError
+    wl = W("b_g", 1, 1, 64, 8, 1, False, (3,))
+    inp = {k: (v.cuda() if v is not None else None) for k, v in make_inputs(wl, 0).items()}
+    with Plan(1, 1, 64, 64, 8, 1, False, (3,)) as pl:
+        o, lse = pl.forward(inp["q"], inp["k"], inp["v"], inp["qg"], inp["kg"], inp["vg"],
+                            want_lse=True)
+        with pytest.raises(SwattnError):
+            pl.backward(inp["q"], inp["k"], inp["v"], o, lse, torch.zeros_like(o),
+                        inp["qg"], inp["kg"], inp["vg"])
