@@ -115,7 +115,7 @@ int swattn_forward(swattn_plan* plan, const void* q, const void* k,
  * Gradients must not overlap each other or any input. The plan's workspace
  * holds per-row statistics, so a plan runs one backward (or forward) at a
  * time. bf16 plans only. Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (fp32
- * plan; n_global > 0 is not implemented yet), HIP.
+ * plan), HIP.
  */
 int swattn_backward(swattn_plan* plan, const void* q, const void* k, const void* v,
                     const void* qg, const void* kg, const void* vg, const void* o,

@@ -11,12 +11,22 @@
 // passes treat them as absent: their log2-LSE is set to +inf (P = 0).
 //
 // Kernels:
-//  * bwd_prep: D_i and the log2-domain LSE (+inf on rows of G), per row.
+//  * bwd_prep: D_i and the log2-domain LSE (+inf on rows of G), per row; the
+//    same statistics of the global rows in a padded [BH][ngp] table; zeros
+//    for the rows of dqg off G.
 //  * bwd_main, band query blocks: 128 query rows of one residue class, Q and
 //    dO in registers, key tiles (K, V) through the ring, the global-column
 //    tile first: dq = s dS K.
 //  * bwd_main, band key blocks: 128 keys of one residue class, K and V in
 //    registers, query tiles (Q, dO, log2-LSE, D) through the ring: dk, dv.
+//  * bwd_main, global-row query blocks: rows of G (Qg, dO) against a chunk of
+//    Kg, Vg: a dQg partial per chunk.
+//  * bwd_main, global-row key blocks: 128 positions of Kg, Vg against the
+//    gathered rows of G: dKg, dVg.
+//  * bwd_main, global-column key blocks: 32 keys of G (K, V) per wave
+//    against a chunk of query positions: partial dK[G], dV[G] terms of the
+//    rows whose band does not hold the key.
+//  * bwd_gred: sums the partials into dqg and into rows G of dk and dv.
 //
 // Score tiles again come out transposed from the MFMA so that the
 // probabilities (and dS) are already the B operand of the next product:
@@ -31,28 +41,49 @@
 
 namespace swattn {
 
+// Per-head band geometry for the global-column blocks.
+struct HeadGeom { int half, right, dil, pad; };
+
 struct BwdParams {
   const void* q;
   const void* k;
   const void* v;
+  const void* qg;
+  const void* kg;
+  const void* vg;
   const void* o;
   const void* dout;
   const float* lse;   // [BH][n], natural log (the forward's output)
   void* dq;
   void* dk;
   void* dv;
+  void* dqg;
+  void* dkg;
+  void* dvg;
   float* lse2;        // [BH][n]: LSE * log2(e), +inf on rows of G
   float* dd;          // [BH][n]: D
+  float* glse2;       // [BH][ngp]: LSE * log2(e) of the global rows (+inf padding)
+  float* gdd;         // [BH][ngp]: D of the global rows (0 padding)
+  float* part_dqg;    // [BH][ng][nsplit][64]: dQg partial per key chunk (unscaled)
+  float* part_gkv;    // [BH][nchunk][ng32][128]: dK[G] (unscaled), dV[G] partial per query chunk
   const TileRec* tiles;
+  const HeadGeom* heads;  // [H]
   int uni_half, uni_right, uni_dil, uni_nqb;
   const int* gidx;
-  int ng;
-  int n;
+  int ng, ngp, ng32;
+  int n, H;
   int causal;
-  int nband_blocks;   // query blocks; the key blocks follow, as many
+  int nsplit, ksplit, nqb, ngroup;  // dQg blocks (as in the forward's global rows)
+  int nchunk;                       // query chunks of the global-column blocks
+  int nkgb;                         // groups of 4 x 32 global keys
+  // block ranges of bwd_main: [0, nq) query blocks, [nq, 2 nq) key blocks,
+  // then dQg blocks, dKg/dVg blocks, global-column blocks
+  int nq, n_gq, n_gkv, n_gcol;
   float c2;           // scale * log2(e)
   float scale;
 };
+
+constexpr int GCOL_QC = 512;  // query positions per global-column block
 
 // ----------------------------------------------------------------------------
 // Row statistics: 8 lanes per row, 8 elements each.
@@ -84,6 +115,23 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
     const bool isg = lo < p.ng && p.gidx[lo] == i;
     p.lse2[row] = isg ? __builtin_inff() : p.lse[row] * LOG2E;
     p.dd[row] = acc;
+    if (isg) {
+      const long bh = row / p.n;
+      p.glse2[bh * p.ngp + lo] = p.lse[row] * LOG2E;
+      p.gdd[bh * p.ngp + lo] = acc;
+    }
+  }
+  // rows of dqg off G are zero (the rows of G come from the reduction)
+  if (row < rows && p.dqg) {
+    const int i = (int)(row % p.n);
+    int lo = 0, hi = p.ng;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (p.gidx[mid] < i) lo = mid + 1;
+      else hi = mid;
+    }
+    if (!(lo < p.ng && p.gidx[lo] == i))
+      *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(p.dqg) + row * HD + 8 * part) = uint4{0, 0, 0, 0};
   }
 }
 
@@ -147,9 +195,12 @@ struct DqWave {
   Acc2 dq;
 };
 
-// One 32-key unit of a K/V tile in LDS (K at kbuf, V at vbuf); `masked` is
-// applied to the raw scores before the exponential.
-template <class MaskFn>
+// One 32-key unit of a K/V tile in LDS (K at kbuf, V at vbuf); `mask` is
+// applied to the raw scores before the exponential. With SPLIT, dS enters
+// its MFMA as a bf16 pair hi + lo (hi = bf16(dS), lo = bf16(dS - hi)), which
+// keeps 16 significant bits: used for the global rows, whose dq sums the
+// terms of every key and cancels the most.
+template <bool SPLIT = false, class MaskFn>
 DEV void dq_unit(DqWave& w, const char* kbuf, const char* vbuf, int kh, const LdsLanes& ll,
                  float c2, bool need_mask, MaskFn&& mask) {
   f32x16 s = score_from(load_kfrag(kbuf, kh, ll), w.qf);
@@ -162,11 +213,18 @@ DEV void dq_unit(DqWave& w, const char* kbuf, const char* vbuf, int kh, const Ld
     const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -w.lse2));
     ds[j] = pj * (dp[j] - w.dd);
   }
-  acc2_mma(w.dq, kt, to_bfrag(ds));
+  const PFrag hi = to_bfrag(ds);
+  acc2_mma(w.dq, kt, hi);
+  if constexpr (SPLIT) {
+    f32x16 lo;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lo[j] = ds[j] - (float)hi.b[j >> 3][j & 7];
+    acc2_mma(w.dq, kt, to_bfrag(lo));
+  }
 }
 
 // The ring for query blocks (K/V tiles, as in the forward).
-template <int S, class Pol>
+template <int S, bool SPLIT = false, class Pol>
 DEV void dq_ring_step(int tb, DqWave& w, const RingCtx& c, const Pol& pol, const DmaLanes<__bf16>& dl,
                       const char* st0, const char* st1, const char* st2) {
   constexpr int TILEB = KT * ElemTraits<__bf16>::ROWB;
@@ -184,8 +242,8 @@ DEV void dq_ring_step(int tb, DqWave& w, const RingCtx& c, const Pol& pol, const
   for (int kh = 0; kh < 2; ++kh) {
     const int ku = k0 + 32 * kh;
     if (!pol.active(ku)) continue;
-    dq_unit(w, cur, cur + TILEB, kh, c.ll, c.c2, !pol.interior(ku),
-            [&](f32x16& s) { pol.template mask<__bf16>(s, ku, c.g); });
+    dq_unit<SPLIT>(w, cur, cur + TILEB, kh, c.ll, c.c2, !pol.interior(ku),
+                   [&](f32x16& s) { pol.template mask<__bf16>(s, ku, c.g); });
   }
 }
 
@@ -424,18 +482,264 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
 }
 
 // ----------------------------------------------------------------------------
-// The main backward kernel: blocks [0, nband_blocks) are query blocks (dq),
-// blocks [nband_blocks, 2 nband_blocks) key blocks (dk, dv) over the same
-// tile schedule.
+// Global rows: dQg partials (query blocks over chunks of Kg, Vg, as in the
+// forward's global-row blocks).
+
+DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st2) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sp = gb % p.nsplit;
+  const int grp = (gb / p.nsplit) % p.ngroup;
+  const int bh = gb / (p.nsplit * p.ngroup);
+  const long base = (long)bh * p.n * ROWB;
+  const int qb = grp * BAND_WAVES + wave;
+  const bool live = qb < p.nqb;
+  const int gi = qb * 32 + (lane & 31);
+  const int pos_q = p.gidx[min(gi, p.ng - 1)];
+  const int gmin = p.gidx[min(qb * 32, p.ng - 1)];
+  const int gmax = p.gidx[min(grp * BAND_WAVES * 32 + BAND_WAVES * 32 - 1, p.ng - 1)];
+  const int k_lo = sp * p.ksplit;
+  int k_hi = min(p.n, k_lo + p.ksplit);
+  if (p.causal) k_hi = min(k_hi, gmax + 1);
+  const int nband = k_hi > k_lo ? (k_hi - k_lo + KT - 1) / KT : 0;
+
+  RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+            (unsigned)(uintptr_t)(lds_void*)st2,
+            reinterpret_cast<const char*>(p.kg) + base, reinterpret_cast<const char*>(p.vg) + base,
+            k_lo, k_hi, nband, 0, 1, wave, lane, g, live, p.c2, {}};
+  lds_lanes_init(c.ll, lane);
+  const GlobPol pol{p.causal ? pos_q : 0x7fffffff - 1, k_hi, gmin, p.causal};
+  DqWave w;
+  acc2_zero(w.dq);
+  if (nband > 0) {
+    const long roff = base + (long)pos_q * ROWB;
+    ring_start<__bf16>(c);
+    load_q(w.qf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.qg) + roff), g);
+    load_q(w.dof, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.dout) + roff), g);
+    w.lse2 = p.glse2[(long)bh * p.ngp + min(gi, p.ngp - 1)];
+    w.dd = p.gdd[(long)bh * p.ngp + min(gi, p.ngp - 1)];
+    wait_vmcnt<0>();
+    DmaLanes<__bf16> dl;
+    dma_lanes_init<__bf16>(dl, 1, lane);
+    for (int tb = 0; tb < nband; tb += 3) {
+      dq_ring_step<0, true>(tb, w, c, pol, dl, st0, st1, st2);
+      if (tb + 1 < nband) dq_ring_step<1, true>(tb + 1, w, c, pol, dl, st0, st1, st2);
+      if (tb + 2 < nband) dq_ring_step<2, true>(tb + 2, w, c, pol, dl, st0, st1, st2);
+    }
+    wait_vmcnt<0>();
+  }
+  if (live && gi < p.ng) {
+    float* po = p.part_dqg + (((long)bh * p.ng + gi) * p.nsplit + sp) * HD;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = w.dq.a[dh][4 * a + e];
+        *reinterpret_cast<f32x4*>(po + 32 * dh + 8 * a + 4 * g) = t;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Global rows: dKg, dVg (key blocks over 128 positions of Kg, Vg; the query
+// tiles are the rows of G, gathered from Qg and dO).
+
+DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  constexpr int TILEB = KT * ROWB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nkb = (p.n + BM - 1) / BM;
+  const int bh = blk / nkb;
+  const int k0 = (blk - bh * nkb) * BM;
+  const long base = (long)bh * p.n * ROWB;
+  const int kw0 = k0 + 32 * wave;
+  const bool wave_live = kw0 < p.n;
+  const int kj = kw0 + (lane & 31);
+  const bool key_ok = kj < p.n;
+  const int pos_k = min(kj, p.n - 1);
+  const long roff = base + (long)pos_k * ROWB;
+  LdsLanes ll;
+  lds_lanes_init(ll, lane);
+  const unsigned a0 = (unsigned)(uintptr_t)(lds_void*)st0;
+  const char* qb = reinterpret_cast<const char*>(p.qg) + base;
+  const char* db = reinterpret_cast<const char*>(p.dout) + base;
+
+  DkvWave w;
+  acc2_zero(w.dk);
+  acc2_zero(w.dv);
+  load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.kg) + roff), g);
+  load_q(w.vf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.vg) + roff), g);
+  for (int t0 = 0; t0 < p.ng; t0 += KT) {
+    int gq[4];
+    gather_rows(gq, p.gidx, t0, p.ng, wave, lane);
+    const int gp = p.gidx[min(t0 + lane, p.ng - 1)];
+    if (t0 > 0) __syncthreads();  // the previous tile is consumed
+    dma_gather(a0, qb, db, gq, wave, lane);
+    const float* src = ((wave & 1) ? p.gdd : p.glse2) + (long)bh * p.ngp + t0 + lane;
+    dma4(src, a0 + (unsigned)(2 * TILEB + 256 * wave));
+    if (tid < KT) gpos[tid] = gp;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (wave_live) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        if (t0 + 32 * kh >= p.ng) continue;
+        dkv_unit(w, st0, kh, ll, p.c2, g, p.causal != 0, [&](f32x16& t) {
+          // causal: key position <= the global row's position
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (pos_k > gpos[32 * kh + key_of_reg<__bf16>(j, g)]) t[j] = -__builtin_inff();
+        });
+      }
+    }
+  }
+  if (wave_live && key_ok) {
+    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dkg) + roff), w.dk, p.scale, g);
+    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dvg) + roff), w.dv, 1.0f, g);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Global columns: the dK[G], dV[G] terms of the non-global rows whose band
+// does not already hold the key (key blocks over query chunks of GCOL_QC
+// positions; wave w holds global keys 32 (4 kg + w) ..).
+
+struct GcolPol {
+  int gpos;      // this lane's global key position
+  int gmin;      // smallest global key position of the wave
+  int qend;      // end of the query chunk (rows past it are clamped copies)
+  int half, right, dil, causal;
+  DEV bool active(int ku) const { return !causal || ku + 31 >= gmin; }
+  DEV bool interior(int) const { return false; }
+  template <class T> DEV void mask(f32x16& t, int ku, int g) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int qi = ku + key_of_reg<T>(j, g);  // query position
+      const int dl = qi - gpos;
+      const bool inband = dl >= -right * dil && dl <= half * dil && dl % dil == 0;
+      if ((causal && gpos > qi) || inband || qi >= qend) t[j] = -__builtin_inff();
+    }
+  }
+};
+
+DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char* st2) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ch = blk % p.nchunk;
+  const int rest = blk / p.nchunk;
+  const int kgb = rest % p.nkgb;
+  const int bh = rest / p.nkgb;
+  const HeadGeom hg = p.heads[bh % p.H];
+  const long base = (long)bh * p.n * ROWB;
+  const int kgi = kgb * BAND_WAVES + wave;  // this wave's group of 32 global keys
+  const bool live = kgi * 32 < p.ng;
+  const int gi = kgi * 32 + (lane & 31);
+  const int gpos = p.gidx[min(gi, p.ng - 1)];
+  const int gmin = p.gidx[min(kgi * 32, p.ng - 1)];
+  const int qbeg = ch * GCOL_QC;
+  const int qend = min(p.n, qbeg + GCOL_QC);
+  const int nband = (qend - qbeg + KT - 1) / KT;
+  const long roff = base + (long)gpos * ROWB;
+
+  RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
+            (unsigned)(uintptr_t)(lds_void*)st2,
+            reinterpret_cast<const char*>(p.q) + base, reinterpret_cast<const char*>(p.dout) + base,
+            qbeg, qend, nband, 0, 1, wave, lane, g, live, p.c2, {}};
+  lds_lanes_init(c.ll, lane);
+  const GcolPol pol{gpos, gmin, qend, hg.half, hg.right, hg.dil, p.causal};
+  const float* lse2 = p.lse2 + (long)bh * p.n;
+  const float* dd = p.dd + (long)bh * p.n;
+
+  DkvWave w;
+  acc2_zero(w.dk);
+  acc2_zero(w.dv);
+  dma_tile<__bf16>(c.a0, c.kb, c.vb, qbeg, qend, 0, 1, wave, lane);
+  dma_stats(c.a0, lse2, dd, qbeg, qend, 0, 1, wave, lane);
+  const int q1 = qbeg + min(1, nband - 1) * KT;
+  dma_tile<__bf16>(c.a1, c.kb, c.vb, q1, qend, 0, 1, wave, lane);
+  dma_stats(c.a1, lse2, dd, q1, qend, 0, 1, wave, lane);
+  load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.k) + roff), g);
+  load_q(w.vf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.v) + roff), g);
+  wait_vmcnt<0>();
+  DmaLanes<__bf16> dl;
+  dma_lanes_init<__bf16>(dl, 1, lane);
+  for (int tb = 0; tb < nband; tb += 3) {
+    dkv_ring_step<0>(tb, w, c, pol, dl, lse2, dd, st0, st1, st2);
+    if (tb + 1 < nband) dkv_ring_step<1>(tb + 1, w, c, pol, dl, lse2, dd, st0, st1, st2);
+    if (tb + 2 < nband) dkv_ring_step<2>(tb + 2, w, c, pol, dl, lse2, dd, st0, st1, st2);
+  }
+  wait_vmcnt<0>();
+  if (live && gi < p.ng) {
+    float* po = p.part_gkv + (((long)bh * p.nchunk + ch) * p.ng32 + gi) * (2 * HD);
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 tk, tv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tk[e] = w.dk.a[dh][4 * a + e];
+          tv[e] = w.dv.a[dh][4 * a + e];
+        }
+        *reinterpret_cast<f32x4*>(po + 32 * dh + 8 * a + 4 * g) = tk;
+        *reinterpret_cast<f32x4*>(po + HD + 32 * dh + 8 * a + 4 * g) = tv;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Reduction for the global tokens, after bwd_main: one block per (b*h, global
+// row). dqg[g] = s * sum of the chunk partials; dk[g], dv[g] gain the
+// global-column terms of every query chunk.
+
+__global__ __launch_bounds__(256) void bwd_gred(BwdParams p) {
+  const int gi = blockIdx.x % p.ng;
+  const long bh = blockIdx.x / p.ng;
+  const int t = threadIdx.x, d = t & 63, part = t >> 6;
+  const long row = bh * p.n + p.gidx[gi];
+  if (part == 0) {
+    const float* src = p.part_dqg + ((bh * p.ng + gi) * p.nsplit) * HD + d;
+    float acc = 0.f;
+    for (int sp = 0; sp < p.nsplit; ++sp) acc += src[(long)sp * HD];
+    reinterpret_cast<__bf16*>(p.dqg)[row * HD + d] = (__bf16)(acc * p.scale);
+  } else if (part <= 2) {
+    const int off = part == 1 ? 0 : HD;
+    const float* src = p.part_gkv + ((bh * p.nchunk) * p.ng32 + gi) * (2 * HD) + off + d;
+    float acc = 0.f;
+    for (int ch = 0; ch < p.nchunk; ++ch) acc += src[(long)ch * p.ng32 * 2 * HD];
+    __bf16* dst = reinterpret_cast<__bf16*>(part == 1 ? p.dk : p.dv) + row * HD + d;
+    *dst = (__bf16)((float)*dst + (part == 1 ? acc * p.scale : acc));
+  }
+}
+
+// ----------------------------------------------------------------------------
+// The main backward kernel: blocks [0, nq) are band query blocks (dq),
+// [nq, 2 nq) band key blocks (dk, dv) over the same tile schedule, then the
+// global-token blocks (dQg partials, dKg/dVg, global-column partials).
 
 __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char st0[QSTAGEB];
   __shared__ __attribute__((aligned(1024))) char st1[QSTAGEB];
   __shared__ __attribute__((aligned(1024))) char st2[QSTAGEB];
   __shared__ int gmeta[2][KT];
-  const int b = blockIdx.x;
-  if (b < p.nband_blocks) bwd_dq_block(p, xcd_remap(b, p.nband_blocks), st0, st1, st2, gmeta);
-  else bwd_dkv_block(p, xcd_remap(b - p.nband_blocks, p.nband_blocks), st0, st1, st2);
+  int b = blockIdx.x;
+  if (b < p.nq) { bwd_dq_block(p, xcd_remap(b, p.nq), st0, st1, st2, gmeta); return; }
+  b -= p.nq;
+  if (b < p.nq) { bwd_dkv_block(p, xcd_remap(b, p.nq), st0, st1, st2); return; }
+  b -= p.nq;
+  if (b < p.n_gq) { bwd_gq_block(p, b, st0, st1, st2); return; }
+  b -= p.n_gq;
+  if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, gmeta[0]); return; }
+  b -= p.n_gkv;
+  bwd_gcol_block(p, b, st0, st1, st2);
 }
 
 }  // namespace swattn

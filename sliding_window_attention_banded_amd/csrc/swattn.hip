@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <new>
 #include <string>
 #include <vector>
@@ -54,6 +55,12 @@ struct swattn_plan {
   float* part_ml;         // [B*H][ng][nsplit][2]
   float* bwd_lse2;        // [B*H][n] backward row statistics (bf16 plans)
   float* bwd_dd;          // [B*H][n]
+  // backward, global tokens (bf16 plans with n_global > 0)
+  int ngp, ng32, nchunk, nkgb, n_gkv, n_gcol;
+  float* bwd_glse2;       // [B*H][ngp], +inf padding
+  float* bwd_gdd;         // [B*H][ngp], 0 padding
+  float* bwd_part_gkv;    // [B*H][nchunk][ng32][128]
+  HeadGeom* bwd_heads;    // [H]
   // measurement hooks
   static constexpr int kMaxTimed = 4096;
   std::vector<hipEvent_t> ev;  // [kMaxTimed][4]: band start/stop, global start/stop
@@ -165,8 +172,28 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const size_t nslot = (size_t)bh * pl->ng * pl->nsplit;
   const size_t sz_po = al(sizeof(float) * HD * nslot);
   const size_t sz_pml = al(sizeof(float) * 2 * nslot);
-  const size_t sz_stat = pl->dtype == SWATTN_BF16 ? al(sizeof(float) * (size_t)bh * p->n) : 0;
-  const size_t total = sz_tiles + sz_g + sz_po + sz_pml + 2 * sz_stat;
+  const bool bwd = pl->dtype == SWATTN_BF16;
+  const size_t sz_stat = bwd ? al(sizeof(float) * (size_t)bh * p->n) : 0;
+  const bool bwd_g = bwd && pl->ng > 0;
+  pl->ngp = bwd_g ? (pl->ng + KT - 1) / KT * KT : 0;
+  pl->ng32 = bwd_g ? (pl->ng + 31) / 32 * 32 : 0;
+  pl->nchunk = bwd_g ? (p->n + GCOL_QC - 1) / GCOL_QC : 0;
+  pl->nkgb = bwd_g ? ((pl->ng + 31) / 32 + BAND_WAVES - 1) / BAND_WAVES : 0;
+  {
+    const long n_gkv = bwd_g ? bh * ((p->n + BM - 1) / BM) : 0;
+    const long n_gcol = bwd_g ? bh * (long)pl->nchunk * pl->nkgb : 0;
+    const long nbwd = 2 * nband_blocks + (bwd_g ? (long)pl->nglob_blocks : 0) + n_gkv + n_gcol;
+    if (nbwd > 0x7fffffffL) {
+      delete pl;
+      return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+    }
+    pl->n_gkv = (int)n_gkv;
+    pl->n_gcol = (int)n_gcol;
+  }
+  const size_t sz_gstat = al(sizeof(float) * (size_t)bh * pl->ngp);
+  const size_t sz_gkv = al(sizeof(float) * (size_t)bh * pl->nchunk * pl->ng32 * 2 * HD);
+  const size_t sz_heads = al(sizeof(HeadGeom) * p->heads);
+  const size_t total = sz_tiles + sz_g + sz_po + sz_pml + 2 * sz_stat + 2 * sz_gstat + sz_gkv + sz_heads;
   e = hipMalloc(&pl->dev_mem, total);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
   char* m = static_cast<char*>(pl->dev_mem);
@@ -175,10 +202,26 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->part_o = reinterpret_cast<float*>(m); m += sz_po;
   pl->part_ml = reinterpret_cast<float*>(m); m += sz_pml;
   pl->bwd_lse2 = sz_stat ? reinterpret_cast<float*>(m) : nullptr; m += sz_stat;
-  pl->bwd_dd = sz_stat ? reinterpret_cast<float*>(m) : nullptr;
+  pl->bwd_dd = sz_stat ? reinterpret_cast<float*>(m) : nullptr; m += sz_stat;
+  pl->bwd_glse2 = reinterpret_cast<float*>(m); m += sz_gstat;
+  pl->bwd_gdd = reinterpret_cast<float*>(m); m += sz_gstat;
+  pl->bwd_part_gkv = reinterpret_cast<float*>(m); m += sz_gkv;
+  pl->bwd_heads = reinterpret_cast<HeadGeom*>(m);
   e = hipSuccess;
   if (!tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess && bwd_g) {
+    // padding rows of the global-row statistics: P = 0 and D = 0 for ever
+    const std::vector<float> inf((size_t)bh * pl->ngp, std::numeric_limits<float>::infinity());
+    const std::vector<float> zero((size_t)bh * pl->ngp, 0.f);
+    e = hipMemcpy(pl->bwd_glse2, inf.data(), sizeof(float) * inf.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(pl->bwd_gdd, zero.data(), sizeof(float) * zero.size(), hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess && bwd) {
+    std::vector<HeadGeom> hg(p->heads);
+    for (int h = 0; h < p->heads; ++h) hg[h] = HeadGeom{half[h], p->causal ? 0 : half[h], dil[h], 0};
+    e = hipMemcpy(pl->bwd_heads, hg.data(), sizeof(HeadGeom) * hg.size(), hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     (void)hipFree(pl->dev_mem);
     delete pl;
@@ -331,7 +374,6 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   g_last_error.clear();
   if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
   if (pl->dtype != SWATTN_BF16) return fail(SWATTN_ERR_UNSUPPORTED, "the backward pass is bf16 only");
-  if (pl->ng > 0) return fail(SWATTN_ERR_UNSUPPORTED, "the backward pass does not support global tokens yet");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(SWATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
   const bool want_g = pl->ng > 0;
@@ -357,21 +399,35 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = 0.125f;
   BwdParams bp;
-  bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.dout = dout; bp.lse = lse;
-  bp.dq = dq; bp.dk = dk; bp.dv = dv;
+  bp.q = q; bp.k = k; bp.v = v; bp.qg = qg; bp.kg = kg; bp.vg = vg;
+  bp.o = o; bp.dout = dout; bp.lse = lse;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dqg = dqg; bp.dkg = dkg; bp.dvg = dvg;
   bp.lse2 = pl->bwd_lse2; bp.dd = pl->bwd_dd;
-  bp.tiles = pl->tiles;
+  bp.glse2 = pl->bwd_glse2; bp.gdd = pl->bwd_gdd;
+  bp.part_dqg = pl->part_o;  // the forward's global-row workspace has this shape
+  bp.part_gkv = pl->bwd_part_gkv;
+  bp.tiles = pl->tiles; bp.heads = pl->bwd_heads;
   bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
   bp.uni_nqb = pl->uni_nqb;
-  bp.gidx = pl->gidx; bp.ng = pl->ng; bp.n = pl->n; bp.causal = pl->causal;
-  bp.nband_blocks = pl->nband_blocks;
+  bp.gidx = pl->gidx; bp.ng = pl->ng; bp.ngp = pl->ngp; bp.ng32 = pl->ng32;
+  bp.n = pl->n; bp.H = pl->H; bp.causal = pl->causal;
+  bp.nsplit = pl->nsplit; bp.ksplit = pl->ksplit; bp.nqb = pl->nqb; bp.ngroup = pl->ngroup;
+  bp.nchunk = pl->nchunk; bp.nkgb = pl->nkgb;
+  bp.nq = pl->nband_blocks;
+  bp.n_gq = pl->ng > 0 ? pl->nglob_blocks : 0;
+  bp.n_gkv = pl->n_gkv; bp.n_gcol = pl->n_gcol;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   const long rows = (long)pl->B * pl->H * pl->n;
   hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st, bp, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch bwd_prep");
-  hipLaunchKernelGGL(bwd_main, dim3(2 * pl->nband_blocks), dim3(256), 0, st, bp);
+  hipLaunchKernelGGL(bwd_main, dim3(2 * bp.nq + bp.n_gq + bp.n_gkv + bp.n_gcol), dim3(256), 0, st, bp);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch bwd_main");
+  if (pl->ng > 0) {
+    hipLaunchKernelGGL(bwd_gred, dim3(pl->ng * pl->B * pl->H), dim3(256), 0, st, bp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch bwd_gred");
+  }
   return SWATTN_OK;
 }

@@ -50,7 +50,14 @@ SMALL = [
     W("b_one", 1, 1, 1, 8, 1),
     W("b_wide", 1, 2, 200, (1000, 602), (1, 1)),
     W("b_window0", 1, 2, 130, (0, 0), (1, 5)),
+    W("b_g1", 2, 2, 300, 64, 1, False, (0,)),
+    W("b_g_mix", 2, 3, 777, (64, 128, 30), (1, 2, 3), False, (0, 17, 400, 776)),
+    W("b_g_causal", 1, 4, 500, (32, 256, 2, 1024), (1, 4, 1, 2), True, (5, 250, 499)),
+    W("b_g_many", 1, 2, 700, (64, 16), (1, 3), False, tuple(range(0, 700, 7))),
+    W("b_g_all", 1, 2, 130, (8, 4), (1, 2), False, tuple(range(130))),
 ]
+
+GRADS = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
 
 
 def _cotangent(wl, seed):
@@ -109,13 +116,18 @@ def test_backward_small(wl, kind):
         dout = _cotangent(wl, seed)
         got = _gpu_grads(wl, inp, dout)
         ref = _oracle_grads(wl, inp, dout)
-        for name, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        for name, a, b in zip(GRADS, got, ref):
+            if b is None:
+                assert a is None
+                continue
             _cmp(a, b, f"{wl.name}/{kind}/{seed}/{name}")
 
 
 @pytest.mark.parametrize("name,bh", [
     ("encoder_b2_h12_n4096_w512", [(0, 0), (1, 11)]),
+    ("encoder_b2_h12_n4096_w512_g1", [(0, 5), (1, 0)]),
     ("arlm_b1_h12_n8192_w512_causal_dil2", [(0, 3), (0, 11)]),
+    ("qa_b4_h12_n4096_w512_g64", [(3, 7)]),
 ])
 @pytest.mark.parametrize("kind", ["normal", "sharp"])
 def test_backward_full_size_slices(name, bh, kind):
@@ -126,17 +138,16 @@ def test_backward_full_size_slices(name, bh, kind):
     got = _gpu_grads(wl, inp, dout)
     refs = _oracle_grads(wl, inp, dout, bh=bh)
     for (b, h), ref in zip(bh, refs):
-        for name_g, a, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        for name_g, a, r in zip(GRADS, got, ref):
+            if r is None:
+                continue
             _cmp(a[b:b + 1, h:h + 1], r, f"{wl.name}[{b},{h}]/{kind}/{name_g}")
 
 
-def test_backward_rejects_global_tokens_for_now():
+def test_backward_rejects_fp32_plans():
     from sliding_window_attention_banded_amd import Plan, SwattnError
-    wl = W("b_g", 1, 1, 64, 8, 1, False, (3,))
-    inp = {k: (v.cuda() if v is not None else None) for k, v in make_inputs(wl, 0).items()}
-    with Plan(1, 1, 64, 64, 8, 1, False, (3,)) as pl:
-        o, lse = pl.forward(inp["q"], inp["k"], inp["v"], inp["qg"], inp["kg"], inp["vg"],
-                            want_lse=True)
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
+    with Plan(1, 1, 64, 64, 8, 1, False, (), torch.float32) as pl:
         with pytest.raises(SwattnError):
-            pl.backward(inp["q"], inp["k"], inp["v"], o, lse, torch.zeros_like(o),
-                        inp["qg"], inp["kg"], inp["vg"])
+            pl.backward(x, x, x, x, lse, x)
