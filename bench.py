@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing-pass", action="store_true",
                     help="skip the per-kernel event pass (e.g. under a profiler)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -108,7 +110,7 @@ def main():
 
     from sliding_window_attention_banded_amd import Plan
     from sliding_window_attention_banded_amd.accounting import (
-        algorithmic_bytes, band_flops, useful_flops)
+        algorithmic_bytes, backward_bytes, backward_flops, band_flops, useful_flops)
     from sliding_window_attention_banded_amd.workloads import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
@@ -201,6 +203,52 @@ def main():
             "hbm_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
             "merge_us": glob_ms * 1e3 if glob_ms else 0.0})
 
+    bwd = None
+    if not args.no_backward and wl.dtype == "bf16":
+        # the backward pass of the same workload: O and LSE of each input set
+        # from one forward, a seeded random cotangent, the gradients written
+        # into preallocated tensors; timed like the forward
+        g = torch.Generator().manual_seed(4321)
+        douts = [torch.randn(tuple(sets[0]["q"].shape), generator=g).to(wl.torch_dtype).to(dev)
+                 for _ in range(min(nsets, 2))]
+        for j in range(nsets):
+            step(j)
+        has_g = bool(wl.global_idx)
+        grads = [tuple(torch.empty_like(sets[0]["q"]) if (i < 3 or has_g) else None
+                       for i in range(6)) for _ in range(2)]
+
+        def bstep(i, rotate=True):
+            j = i % nsets if rotate else 0
+            x = sets[j]
+            plan.backward(x["q"], x["k"], x["v"], outs[j], lses[j], douts[j % len(douts)],
+                          x["qg"], x["kg"], x["vg"], grads=grads[i % 2], stream=stream)
+
+        def btimed(k, rotate):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(k):
+                bstep(i, rotate)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / k
+
+        for i in range(args.warmup):
+            bstep(i)
+        bms = btimed(args.steps, True)
+        bms_warm = btimed(args.steps, False)
+        bf_b, bb_b = backward_flops(wl), backward_bytes(wl)
+        print(f"[bench] backward {bms * 1e3:.2f} us/step (rotating), {bms_warm * 1e3:.2f} us/step "
+              f"(warm)", file=sys.stderr, flush=True)
+        bwd = {"ms_per_step": bms, "tflops": bf_b / (bms * 1e-3) / 1e12,
+               "gbs": bb_b / (bms * 1e-3) / 1e9,
+               "algorithmic_gflop": bf_b / 1e9, "algorithmic_bytes": bb_b,
+               "mfma_frac": bf_b / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "hbm_frac": bb_b / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "warm": {"ms_per_step": bms_warm, "tflops": bf_b / (bms_warm * 1e-3) / 1e12},
+               "tokens_per_s": tokens / (bms * 1e-3)}
+
     line = {
         "metric": METRIC,
         "value": bf / (ms * 1e-3) / 1e12,
@@ -220,6 +268,7 @@ def main():
                  "tokens_per_s": tokens / (ms_warm * 1e-3)},
         "input_sets": nsets,
         "roofline": roof,
+        "backward": bwd,
         "cpu_baseline": None,
     }
     plan.close()

@@ -17,7 +17,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["band_keys_per_row", "band_flops", "useful_flops",
-           "algorithmic_bytes", "global_column_extras"]
+           "algorithmic_bytes", "global_column_extras", "backward_flops", "backward_bytes"]
 
 
 def band_keys_per_row(n, window, dilation, causal):
@@ -85,4 +85,25 @@ def algorithmic_bytes(wl, with_lse=True):
         b += 2 * bh * wl.n * wl.d * es + bh * len(wl.global_idx) * wl.d * es
     if with_lse:
         b += 4 * bh * wl.n
+    return b
+
+
+def backward_flops(wl):
+    """Algorithmic FLOPs of the backward pass: five products per attended
+    (row, key) pair -- the recomputed scores q.k, dP = dO.v, and the three
+    gradient products dq += dS k, dk += dS q, dv += P dO -- at 2*d each,
+    i.e. 2.5 times the forward's 4*d per pair."""
+    return useful_flops(wl) * 10 // 4
+
+
+def backward_bytes(wl):
+    """Bytes that must cross HBM once in the backward pass: Q, K, V, O, dO and
+    the LSE read, dQ, dK, dV written; with global tokens also Kg, Vg read in
+    full with the Qg rows, and dQg, dKg, dVg written in full."""
+    es = 2 if wl.dtype == "bf16" else 4
+    bh = wl.batch * wl.heads
+    row = wl.d * es
+    b = bh * wl.n * (5 * row + 4 + 3 * row)
+    if wl.global_idx:
+        b += bh * wl.n * (2 * row + 3 * row) + bh * len(wl.global_idx) * row
     return b
