@@ -33,8 +33,10 @@ Readings taken where the page is silent or garbled:
       regular K[G], V[G], so each row is one softmax over one projection set.
 * R6  a global key inside a row's band counts once (set union).
 * R7  causal applies to global rows and columns too.
-* R8  one G shared by every batch item and head; dilation applies to the band
-      only.
+* R8  G is shared by every head; dilation applies to the band only. G is one
+      set for all batch items, or one set per batch item (the QA setting of
+      section 3-1: each example's question tokens are its global tokens);
+      ``global_idx`` then lists B sequences.
 """
 
 from __future__ import annotations
@@ -110,6 +112,25 @@ def _masked_softmax_rows(qr, k, v, mask, scale):
     return o, lse
 
 
+def _per_batch_globals(global_idx, B, n):
+    """G of every batch item: a flat sequence (shared) or B sequences."""
+    items = list(global_idx) if not isinstance(global_idx, np.ndarray) else list(global_idx.reshape(-1))
+    per = bool(items) and all(isinstance(x, (list, tuple, np.ndarray)) for x in items)
+    if per:
+        if len(items) != B:
+            raise ValueError("per-example global_idx needs one sequence per batch item")
+        gls = [np.asarray(x, dtype=np.int64).reshape(-1) for x in items]
+    else:
+        gls = [np.asarray(items, dtype=np.int64).reshape(-1)] * B
+    for gl in gls:
+        if gl.size:
+            if len(np.unique(gl)) != gl.size:
+                raise ValueError("global_idx repeats an index")
+            if gl.min() < 0 or gl.max() >= n:
+                raise ValueError("global_idx out of range")
+    return gls
+
+
 def attention(q, k, v, qg=None, kg=None, vg=None, *, window, dilation,
               causal=False, global_idx=(), rows=None, row_block=1024):
     """Oracle forward: O [B,H,R,d] and LSE [B,H,R] in float64.
@@ -117,8 +138,9 @@ def attention(q, k, v, qg=None, kg=None, vg=None, *, window, dilation,
     ``q, k, v`` (and ``qg, kg, vg`` when G is not empty) are [B,H,n,d] arrays;
     they are upcast to float64 exactly. ``window`` and ``dilation`` are per
     head (sequences of length H) or scalars. ``rows`` selects which rows to
-    compute (default: all n); R = len(rows). ``global_idx`` may be unsorted
-    but must not repeat.
+    compute (default: all n); R = len(rows). ``global_idx`` (one set for
+    every batch item, or B sets: reading R8) may be unsorted but must not
+    repeat.
 
     Each row block builds the explicit [rows x n] mask and evaluates the
     masked softmax directly (section 3-1; readings R1-R8 above).
@@ -129,12 +151,8 @@ def attention(q, k, v, qg=None, kg=None, vg=None, *, window, dilation,
     B, H, n, d = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one [B,H,n,d] shape")
-    gl = np.asarray(global_idx, dtype=np.int64).reshape(-1)
-    if gl.size:
-        if len(np.unique(gl)) != gl.size:
-            raise ValueError("global_idx repeats an index")
-        if gl.min() < 0 or gl.max() >= n:
-            raise ValueError("global_idx out of range")
+    gls = _per_batch_globals(global_idx, B, n)
+    if any(gl.size for gl in gls):
         qg = np.asarray(qg, dtype=np.float64)
         kg = np.asarray(kg, dtype=np.float64)
         vg = np.asarray(vg, dtype=np.float64)
@@ -144,14 +162,15 @@ def attention(q, k, v, qg=None, kg=None, vg=None, *, window, dilation,
     win = np.broadcast_to(np.asarray(window, dtype=np.int64), (H,))
     dil = np.broadcast_to(np.asarray(dilation, dtype=np.int64), (H,))
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
-    isg = np.zeros(n, dtype=bool)
-    isg[gl] = True
     scale = 1.0 / np.sqrt(d)
 
     R = rows.size
     o = np.zeros((B, H, R, d), dtype=np.float64)
     lse = np.zeros((B, H, R), dtype=np.float64)
     for b in range(B):
+        gl = gls[b]
+        isg = np.zeros(n, dtype=bool)
+        isg[gl] = True
         for h in range(H):
             for s0 in range(0, R, row_block):
                 rb = rows[s0:s0 + row_block]
@@ -193,7 +212,8 @@ def attention_backward(q, k, v, qg, kg, vg, do, *, window, dilation, causal=Fals
     """Oracle backward: gradients of every input for the cotangent ``do`` of O.
 
     Returns (dq, dk, dv, dqg, dkg, dvg), float64 arrays of q's shape; the
-    global-projection gradients are None when G is empty. A non-global row i
+    global-projection gradients are None when G is empty (for every batch
+    item). ``global_idx`` is one set or B sets, as in ``attention``. A non-global row i
     depends on q_i and on k_j, v_j for j in A(i); a global row g on qg_g and
     on kg_j, vg_j for every allowed j (section 3-1, readings R1-R8). Rows of G
     take their output from the global projections only, so dq is zero there,
@@ -207,12 +227,9 @@ def attention_backward(q, k, v, qg, kg, vg, do, *, window, dilation, causal=Fals
     for t in (k, v, do):
         if t.shape != q.shape:
             raise ValueError("k, v, do must have q's [B,H,n,d] shape")
-    gl = np.asarray(global_idx, dtype=np.int64).reshape(-1)
-    if gl.size:
-        if len(np.unique(gl)) != gl.size:
-            raise ValueError("global_idx repeats an index")
-        if gl.min() < 0 or gl.max() >= n:
-            raise ValueError("global_idx out of range")
+    gls = _per_batch_globals(global_idx, B, n)
+    anyg = any(gl.size for gl in gls)
+    if anyg:
         qg = np.asarray(qg, dtype=np.float64)
         kg = np.asarray(kg, dtype=np.float64)
         vg = np.asarray(vg, dtype=np.float64)
@@ -221,17 +238,18 @@ def attention_backward(q, k, v, qg, kg, vg, do, *, window, dilation, causal=Fals
                 raise ValueError("qg, kg, vg must have q's shape")
     win = np.broadcast_to(np.asarray(window, dtype=np.int64), (H,))
     dil = np.broadcast_to(np.asarray(dilation, dtype=np.int64), (H,))
-    isg = np.zeros(n, dtype=bool)
-    isg[gl] = True
     scale = 1.0 / np.sqrt(d)
 
     dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
-    if gl.size:
+    if anyg:
         dqg, dkg, dvg = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
     else:
         dqg = dkg = dvg = None
     rows = np.arange(n)
     for b in range(B):
+        gl = gls[b]
+        isg = np.zeros(n, dtype=bool)
+        isg[gl] = True
         for h in range(H):
             for s0 in range(0, n, row_block):
                 rb = rows[s0:s0 + row_block]
