@@ -52,7 +52,7 @@ def cpu_baseline(wl, seconds):
 
     from oracle import attention
     from sliding_window_attention_banded_amd.accounting import band_keys_per_row
-    from sliding_window_attention_banded_amd.workloads import make_inputs
+    from sliding_window_attention_banded_amd.workloads import item_globals, make_inputs
 
     inp = make_inputs(wl, 0)
     f64 = {k: (v.double().numpy() if v is not None else None) for k, v in inp.items()}
@@ -64,7 +64,7 @@ def cpu_baseline(wl, seconds):
             attention(sl(f64["q"]), sl(f64["k"]), sl(f64["v"]), sl(f64["qg"]),
                       sl(f64["kg"]), sl(f64["vg"]), window=wl.window[h],
                       dilation=wl.dilation[h], causal=wl.causal,
-                      global_idx=list(wl.global_idx))
+                      global_idx=list(item_globals(wl)[b]))
             done_flops += 4 * wl.d * int(band_keys_per_row(wl.n, wl.window[h],
                                                            wl.dilation[h], wl.causal).sum())
             done_rows += wl.n
@@ -111,9 +111,11 @@ def main():
     from sliding_window_attention_banded_amd import Plan
     from sliding_window_attention_banded_amd.accounting import (
         algorithmic_bytes, backward_bytes, backward_flops, band_flops, useful_flops)
-    from sliding_window_attention_banded_amd.workloads import WORKLOADS, make_inputs
+    from sliding_window_attention_banded_amd.workloads import (
+        WORKLOADS, has_globals, item_globals, make_inputs)
 
     wl = WORKLOADS[args.workload]
+    per_item_g = len(set(item_globals(wl))) > 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: building inputs", file=sys.stderr, flush=True)
@@ -213,7 +215,7 @@ def main():
                  for _ in range(min(nsets, 2))]
         for j in range(nsets):
             step(j)
-        has_g = bool(wl.global_idx)
+        has_g = has_globals(wl)
         grads = [tuple(torch.empty_like(sets[0]["q"]) if (i < 3 or has_g) else None
                        for i in range(6)) for _ in range(2)]
 
@@ -260,7 +262,8 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
                    "seq_len": wl.n, "head_dim": wl.d, "window": wl.window[0],
                    "dilation": list(wl.dilation), "causal": wl.causal,
-                   "n_global": len(wl.global_idx), "parallelism": "none (1 GPU)"},
+                   "n_global": [len(g) for g in item_globals(wl)] if per_item_g else len(wl.global_idx),
+                   "parallelism": "none (1 GPU)"},
         "tokens_per_s": tokens / (ms * 1e-3),
         "useful_tflops": useful_flops(wl) / (ms * 1e-3) / 1e12,
         "algorithmic_gbs": algorithmic_bytes(wl) / (ms * 1e-3) / 1e9,

@@ -60,6 +60,14 @@ typedef struct swattn_params {
   const int32_t* global_idx;   /* host [n_global]: positions of G, each in [0, n), no repeats, any order */
   int32_t n_global;            /* 0 <= |G| <= n; global_idx may be NULL when 0 */
   int32_t dtype;               /* SWATTN_BF16 or SWATTN_FP32 */
+  const int32_t* global_offsets; /* host [batch+1] or NULL. NULL: global_idx is one set G
+                                    shared by every batch item. Otherwise batch item b has
+                                    its own set global_idx[global_offsets[b] ..
+                                    global_offsets[b+1]) (each in [0, n), no repeats within
+                                    an item, any order, at most n per item; offsets start
+                                    at 0, never decrease and end at n_global <= batch*n):
+                                    the QA setting of section 3-1, where each example's
+                                    question tokens are its global tokens. */
 } swattn_params;
 
 typedef struct swattn_plan swattn_plan;

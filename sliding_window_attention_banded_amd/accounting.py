@@ -60,29 +60,36 @@ def global_column_extras(n, window, dilation, causal, global_idx):
 
 def useful_flops(wl):
     """4*d*(keys actually attended): band keys of non-global rows, plus the
-    global columns outside their bands, plus every key of each global row."""
-    g = np.asarray(wl.global_idx, dtype=np.int64)
+    global columns outside their bands, plus every key of each global row
+    (per batch item, with that item's global set)."""
+    from .workloads import item_globals
+    sets = item_globals(wl)
     tot = 0
-    for h in range(wl.heads):
-        kb = band_keys_per_row(wl.n, wl.window[h], wl.dilation[h], wl.causal)
-        ex = global_column_extras(wl.n, wl.window[h], wl.dilation[h],
-                                  wl.causal, wl.global_idx)
-        keep = np.ones(wl.n, dtype=bool)
-        keep[g] = False
-        tot += int(kb[keep].sum() + ex.sum())
-        if g.size:
-            tot += int((g + 1).sum()) if wl.causal else int(g.size * wl.n)
-    return 4 * wl.d * wl.batch * tot
+    for gs in set(sets):
+        mult = sets.count(gs)
+        g = np.asarray(gs, dtype=np.int64)
+        for h in range(wl.heads):
+            kb = band_keys_per_row(wl.n, wl.window[h], wl.dilation[h], wl.causal)
+            ex = global_column_extras(wl.n, wl.window[h], wl.dilation[h], wl.causal, gs)
+            keep = np.ones(wl.n, dtype=bool)
+            keep[g] = False
+            t = int(kb[keep].sum() + ex.sum())
+            if g.size:
+                t += int((g + 1).sum()) if wl.causal else int(g.size * wl.n)
+            tot += mult * t
+    return 4 * wl.d * tot
 
 
 def algorithmic_bytes(wl, with_lse=True):
     """Bytes that must cross HBM once: Q, K, V read and O written; with
     global tokens also Kg, Vg in full and the Qg rows; plus the fp32 LSE."""
+    from .workloads import item_globals
     es = 2 if wl.dtype == "bf16" else 4
     bh = wl.batch * wl.heads
     b = 4 * bh * wl.n * wl.d * es
-    if wl.global_idx:
-        b += 2 * bh * wl.n * wl.d * es + bh * len(wl.global_idx) * wl.d * es
+    for gs in item_globals(wl):  # Kg, Vg of items with global tokens, and their Qg rows
+        if gs:
+            b += wl.heads * (2 * wl.n + len(gs)) * wl.d * es
     if with_lse:
         b += 4 * bh * wl.n
     return b
@@ -100,10 +107,12 @@ def backward_bytes(wl):
     """Bytes that must cross HBM once in the backward pass: Q, K, V, O, dO and
     the LSE read, dQ, dK, dV written; with global tokens also Kg, Vg read in
     full with the Qg rows, and dQg, dKg, dVg written in full."""
+    from .workloads import item_globals
     es = 2 if wl.dtype == "bf16" else 4
     bh = wl.batch * wl.heads
     row = wl.d * es
     b = bh * wl.n * (5 * row + 4 + 3 * row)
-    if wl.global_idx:
-        b += bh * wl.n * (2 * row + 3 * row) + bh * len(wl.global_idx) * row
+    for gs in item_globals(wl):
+        if gs:
+            b += wl.heads * (wl.n * (2 * row + 3 * row) + len(gs) * row)
     return b

@@ -36,7 +36,8 @@ class _Params(ctypes.Structure):
                 ("dilation", ctypes.POINTER(ctypes.c_int32)),
                 ("causal", ctypes.c_int32),
                 ("global_idx", ctypes.POINTER(ctypes.c_int32)),
-                ("n_global", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("n_global", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("global_offsets", ctypes.POINTER(ctypes.c_int32))]
 
 
 def library_path():
@@ -93,7 +94,8 @@ class Plan:
 
     ``window`` and ``dilation`` are per head (a scalar is broadcast);
     ``global_idx`` lists the global-token positions shared by all batch items
-    and heads. Tensors are [B, H, n, 64] contiguous CUDA tensors in ``dtype``.
+    and heads, or gives one such list per batch item. Tensors are
+    [B, H, n, 64] contiguous CUDA tensors in ``dtype``.
     """
 
     def __init__(self, batch, heads, n, d=64, window=512, dilation=1,
@@ -105,16 +107,33 @@ class Plan:
         dil = [int(dilation)] * heads if isinstance(dilation, int) else [int(x) for x in dilation]
         if len(win) != heads or len(dil) != heads:
             raise SwattnError(ERR_INVALID_ARG, "window/dilation need one entry per head")
-        gl = [int(x) for x in global_idx]
+        items = list(global_idx)
+        per_item = bool(items) and all(isinstance(x, (list, tuple)) for x in items)
+        if per_item:
+            if len(items) != batch:
+                raise SwattnError(ERR_INVALID_ARG, "per-example global_idx needs one list per batch item")
+            sets = [[int(x) for x in g] for g in items]
+            gl = [x for g in sets for x in g]
+            offs = [0]
+            for g in sets:
+                offs.append(offs[-1] + len(g))
+            self.global_idx = tuple(tuple(g) for g in sets)
+        else:
+            gl = [int(x) for x in items]
+            offs = None
+            self.global_idx = tuple(gl)
+        self.has_globals = bool(gl)
         self.batch, self.heads, self.n, self.d = batch, heads, n, d
         self.window, self.dilation, self.causal = tuple(win), tuple(dil), bool(causal)
-        self.global_idx, self.dtype = tuple(gl), dtype
+        self.dtype = dtype
         W = (ctypes.c_int32 * heads)(*win)
         D = (ctypes.c_int32 * heads)(*dil)
         G = (ctypes.c_int32 * max(1, len(gl)))(*gl) if gl else None
+        O = (ctypes.c_int32 * len(offs))(*offs) if offs else None
         p = _Params(batch, heads, n, d, W, D, int(bool(causal)),
                     ctypes.cast(G, ctypes.POINTER(ctypes.c_int32)) if G else None,
-                    len(gl), _DT[dtype])
+                    len(gl), _DT[dtype],
+                    ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O else None)
         h = ctypes.c_void_p()
         _check(self._lib, self._lib.swattn_create(ctypes.byref(p), ctypes.byref(h)),
                "swattn_create")
@@ -165,7 +184,7 @@ class Plan:
         if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
                 or tuple(lse.shape) != (self.batch, self.heads, self.n):
             raise SwattnError(ERR_INVALID_ARG, "lse must be contiguous fp32 [B, H, n]")
-        has_g = bool(self.global_idx)
+        has_g = self.has_globals
         if grads is None:
             grads = tuple(torch.empty_like(q) if (i < 3 or has_g) else None for i in range(6))
         names = ("dq", "dk", "dv", "dqg", "dkg", "dvg")

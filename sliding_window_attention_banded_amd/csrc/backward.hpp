@@ -69,8 +69,9 @@ struct BwdParams {
   const TileRec* tiles;
   const HeadGeom* heads;  // [H]
   int uni_half, uni_right, uni_dil, uni_nqb;
-  const int* gidx;
-  int ng, ngp, ng32;
+  const int* gidx;        // as in BandParams: one set, or per-item sets
+  const int* goff;        // [B+1] or NULL
+  int ng, ngp, ng32;      // ng: |G| or the largest per-item |G|
   int n, H;
   int causal;
   int nsplit, ksplit, nqb, ngroup;  // dQg blocks (as in the forward's global rows)
@@ -103,16 +104,18 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
+  const long rowc = row < rows ? row : rows - 1;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, (int)(rowc / p.n / p.H));
   if (row < rows && part == 0) {
     const int i = (int)(row % p.n);
-    // G is sorted: binary search for i
-    int lo = 0, hi = p.ng;
+    // each set is sorted: binary search for i
+    int lo = 0, hi = gs.n;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (p.gidx[mid] < i) lo = mid + 1;
+      if (gs.idx[mid] < i) lo = mid + 1;
       else hi = mid;
     }
-    const bool isg = lo < p.ng && p.gidx[lo] == i;
+    const bool isg = lo < gs.n && gs.idx[lo] == i;
     p.lse2[row] = isg ? __builtin_inff() : p.lse[row] * LOG2E;
     p.dd[row] = acc;
     if (isg) {
@@ -124,13 +127,13 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
   // rows of dqg off G are zero (the rows of G come from the reduction)
   if (row < rows && p.dqg) {
     const int i = (int)(row % p.n);
-    int lo = 0, hi = p.ng;
+    int lo = 0, hi = gs.n;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (p.gidx[mid] < i) lo = mid + 1;
+      if (gs.idx[mid] < i) lo = mid + 1;
       else hi = mid;
     }
-    if (!(lo < p.ng && p.gidx[lo] == i))
+    if (!(lo < gs.n && gs.idx[lo] == i))
       *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(p.dqg) + row * HD + 8 * part) = uint4{0, 0, 0, 0};
   }
 }
@@ -258,11 +261,14 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   bp.tiles = p.tiles; bp.uni_half = p.uni_half; bp.uni_right = p.uni_right;
   bp.uni_dil = p.uni_dil; bp.uni_nqb = p.uni_nqb; bp.n = p.n;
   const TileRec td = decode_tile(bp, tile);
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, td.bh / p.H);
+  const int* gix = gs.idx;
+  const int ngb = gs.n;
   int gq[4] = {0, 0, 0, 0};
   int gm = 0;
-  if (p.ng > 0) {
-    gather_rows(gq, p.gidx, 0, p.ng, wave, lane);
-    gm = p.gidx[min(lane, p.ng - 1)];
+  if (ngb > 0) {
+    gather_rows(gq, gix, 0, ngb, wave, lane);
+    gm = gix[min(lane, ngb - 1)];
   }
   const int bh = td.bh, r = td.r, q0 = td.q0, nr = td.nr;
   if (q0 >= nr) return;
@@ -289,21 +295,21 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   DqWave w;
   acc2_zero(w.dq);
   const long roff = base + (long)pos_q * ROWB;
-  if (p.ng > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
+  if (ngb > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
   ring_start<__bf16>(c);
   load_q(w.qf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.q) + roff), g);
   load_q(w.dof, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.dout) + roff), g);
   w.lse2 = p.lse2[(long)bh * p.n + pos_q];
   w.dd = p.dd[(long)bh * p.n + pos_q];
-  if (p.ng > 0) {
-    if (tid < KT) gmeta_write(gmeta, gm, tid < p.ng, r, dil, tid);
+  if (ngb > 0) {
+    if (tid < KT) gmeta_write(gmeta, gm, tid < ngb, r, dil, tid);
     wait_vmcnt<0>();
     __syncthreads();
     for (int t0 = 0;;) {
       if (wave_live) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-          if (t0 + 32 * kh >= p.ng) continue;
+          if (t0 + 32 * kh >= ngb) continue;
           dq_unit(w, st2, st2 + TILEB, kh, c.ll, p.c2, true, [&](f32x16& s) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -316,12 +322,12 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
         }
       }
       t0 += KT;
-      if (t0 >= p.ng) break;
-      gather_rows(gq, p.gidx, t0, p.ng, wave, lane);
-      gm = p.gidx[min(t0 + lane, p.ng - 1)];
+      if (t0 >= ngb) break;
+      gather_rows(gq, gix, t0, ngb, wave, lane);
+      gm = gix[min(t0 + lane, ngb - 1)];
       __syncthreads();
       dma_gather(c.a2, kb, vb, gq, wave, lane);
-      if (tid < KT) gmeta_write(gmeta, gm, t0 + tid < p.ng, r, dil, tid);
+      if (tid < KT) gmeta_write(gmeta, gm, t0 + tid < ngb, r, dil, tid);
       wait_vmcnt<0>();
       __syncthreads();
     }
@@ -494,12 +500,14 @@ DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st
   const int grp = (gb / p.nsplit) % p.ngroup;
   const int bh = gb / (p.nsplit * p.ngroup);
   const long base = (long)bh * p.n * ROWB;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  if (gs.n <= grp * BAND_WAVES * 32) return;  // no rows of this item's set in this group
   const int qb = grp * BAND_WAVES + wave;
-  const bool live = qb < p.nqb;
+  const bool live = qb * 32 < gs.n;
   const int gi = qb * 32 + (lane & 31);
-  const int pos_q = p.gidx[min(gi, p.ng - 1)];
-  const int gmin = p.gidx[min(qb * 32, p.ng - 1)];
-  const int gmax = p.gidx[min(grp * BAND_WAVES * 32 + BAND_WAVES * 32 - 1, p.ng - 1)];
+  const int pos_q = gs.idx[min(gi, gs.n - 1)];
+  const int gmin = gs.idx[min(qb * 32, gs.n - 1)];
+  const int gmax = gs.idx[min(grp * BAND_WAVES * 32 + BAND_WAVES * 32 - 1, gs.n - 1)];
   const int k_lo = sp * p.ksplit;
   int k_hi = min(p.n, k_lo + p.ksplit);
   if (p.causal) k_hi = min(k_hi, gmax + 1);
@@ -530,7 +538,7 @@ DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st
     }
     wait_vmcnt<0>();
   }
-  if (live && gi < p.ng) {
+  if (live && gi < gs.n) {
     float* po = p.part_dqg + (((long)bh * p.ng + gi) * p.nsplit + sp) * HD;
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh)
@@ -557,6 +565,8 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
   const int nkb = (p.n + BM - 1) / BM;
   const int bh = blk / nkb;
   const int k0 = (blk - bh * nkb) * BM;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  const int ngb = gs.n;
   const long base = (long)bh * p.n * ROWB;
   const int kw0 = k0 + 32 * wave;
   const bool wave_live = kw0 < p.n;
@@ -575,10 +585,10 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
   acc2_zero(w.dv);
   load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.kg) + roff), g);
   load_q(w.vf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.vg) + roff), g);
-  for (int t0 = 0; t0 < p.ng; t0 += KT) {
+  for (int t0 = 0; t0 < ngb; t0 += KT) {
     int gq[4];
-    gather_rows(gq, p.gidx, t0, p.ng, wave, lane);
-    const int gp = p.gidx[min(t0 + lane, p.ng - 1)];
+    gather_rows(gq, gs.idx, t0, ngb, wave, lane);
+    const int gp = gs.idx[min(t0 + lane, ngb - 1)];
     if (t0 > 0) __syncthreads();  // the previous tile is consumed
     dma_gather(a0, qb, db, gq, wave, lane);
     const float* src = ((wave & 1) ? p.gdd : p.glse2) + (long)bh * p.ngp + t0 + lane;
@@ -589,7 +599,7 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
     if (wave_live) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        if (t0 + 32 * kh >= p.ng) continue;
+        if (t0 + 32 * kh >= ngb) continue;
         dkv_unit(w, st0, kh, ll, p.c2, g, p.causal != 0, [&](f32x16& t) {
           // causal: key position <= the global row's position
 #pragma unroll
@@ -639,11 +649,13 @@ DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char*
   const int bh = rest / p.nkgb;
   const HeadGeom hg = p.heads[bh % p.H];
   const long base = (long)bh * p.n * ROWB;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  if (gs.n <= kgb * BAND_WAVES * 32) return;  // no keys of this item's set in this group
   const int kgi = kgb * BAND_WAVES + wave;  // this wave's group of 32 global keys
-  const bool live = kgi * 32 < p.ng;
+  const bool live = kgi * 32 < gs.n;
   const int gi = kgi * 32 + (lane & 31);
-  const int gpos = p.gidx[min(gi, p.ng - 1)];
-  const int gmin = p.gidx[min(kgi * 32, p.ng - 1)];
+  const int gpos = gs.idx[min(gi, gs.n - 1)];
+  const int gmin = gs.idx[min(kgi * 32, gs.n - 1)];
   const int qbeg = ch * GCOL_QC;
   const int qend = min(p.n, qbeg + GCOL_QC);
   const int nband = (qend - qbeg + KT - 1) / KT;
@@ -677,7 +689,7 @@ DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char*
     if (tb + 2 < nband) dkv_ring_step<2>(tb + 2, w, c, pol, dl, lse2, dd, st0, st1, st2);
   }
   wait_vmcnt<0>();
-  if (live && gi < p.ng) {
+  if (live && gi < gs.n) {
     float* po = p.part_gkv + (((long)bh * p.nchunk + ch) * p.ng32 + gi) * (2 * HD);
 #pragma unroll
     for (int dh = 0; dh < 2; ++dh)
@@ -703,8 +715,10 @@ DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char*
 __global__ __launch_bounds__(256) void bwd_gred(BwdParams p) {
   const int gi = blockIdx.x % p.ng;
   const long bh = blockIdx.x / p.ng;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, (int)(bh / p.H));
+  if (gi >= gs.n) return;
   const int t = threadIdx.x, d = t & 63, part = t >> 6;
-  const long row = bh * p.n + p.gidx[gi];
+  const long row = bh * p.n + gs.idx[gi];
   if (part == 0) {
     const float* src = p.part_dqg + ((bh * p.ng + gi) * p.nsplit) * HD + d;
     float acc = 0.f;

@@ -82,8 +82,9 @@ struct BandParams {
   // (B*H, uni_dil, uni_nqb)
   const TileRec* tiles;
   int uni_half, uni_right, uni_dil, uni_nqb;
-  const int* gidx;       // sorted G, [ng]
-  int ng;
+  const int* gidx;       // sorted G: one set, or the batch items' sets one after another
+  const int* goff;       // [B+1] offsets of the per-item sets in gidx, or NULL (one set)
+  int ng;                // |G| (one set), or the largest per-item |G|
   int H;
   int n;
   int causal;
@@ -98,6 +99,8 @@ struct GlobalParams {
   void* o;
   float* lse;
   const int* gidx;
+  const int* goff;  // as in BandParams
+  int H;
   float* part_o;  // [BH][ng][nsplit][64]
   float* part_ml; // [BH][ng][nsplit][2]  (max, sum)
   int ng;
@@ -110,6 +113,18 @@ struct GlobalParams {
   float c2;
   float scale;
 };
+
+// The global tokens of batch item b: the shared set, or the b-th per-item
+// set (its size may be anything up to ng, 0 included).
+struct GSet {
+  const int* idx;
+  int n;
+};
+DEV GSet batch_gset(const int* gidx, const int* goff, int ng, int b) {
+  if (!goff) return GSet{gidx, ng};
+  const int o0 = goff[b];
+  return GSet{gidx + o0, goff[b + 1] - o0};
+}
 
 // ----------------------------------------------------------------------------
 // small helpers
@@ -838,14 +853,17 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // The indices of the first global-column tile do not depend on the tile
-  // record: their loads go out right behind its scalar load.
+  // The indices of the first global-column tile go out right behind the
+  // tile record's scalar load (with per-item sets, behind the set's offsets).
   const TileRec td = decode_tile(p, tile);
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, td.bh / p.H);
+  const int* gix = gs.idx;
+  const int ngb = gs.n;
   int gq[4] = {0, 0, 0, 0};
   int gm = 0;
-  if (BF16 && p.ng > 0) {
-    gather_rows(gq, p.gidx, 0, p.ng, wave, lane);
-    gm = p.gidx[min(lane, p.ng - 1)];
+  if (BF16 && ngb > 0) {
+    gather_rows(gq, gix, 0, ngb, wave, lane);
+    gm = gix[min(lane, ngb - 1)];
   }
   const int bh = td.bh, r = td.r, q0 = td.q0, nr = td.nr;
   if (q0 >= nr) return;  // an empty residue block (uniform decode only)
@@ -883,23 +901,23 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
     // global-column tile into stage 2, band tiles 0 and 1 into stages 0 and
     // 1, and Q. (The gather goes first: the compiler waits for the indices
     // it needs with a count that only knows its own loads.)
-    if (p.ng > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
+    if (ngb > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
     ring_start<T>(c);
     load_q(qf, qrow, g);
-    if (p.ng > 0) {
-      if (tid < KT) gmeta_write(gmeta, gm, tid < p.ng, r, dil, tid);
+    if (ngb > 0) {
+      if (tid < KT) gmeta_write(gmeta, gm, tid < ngb, r, dil, tid);
       wait_vmcnt<0>();
       __syncthreads();
-      if (wave_live) glob_cols_tile<T>(acc, qf, c, st2, gmeta, 0, p.ng, qi, half, right, lim);
-      for (int t0 = KT; t0 < p.ng; t0 += KT) {  // more than 64 global tokens
-        gather_rows(gq, p.gidx, t0, p.ng, wave, lane);
-        gm = p.gidx[min(t0 + lane, p.ng - 1)];
+      if (wave_live) glob_cols_tile<T>(acc, qf, c, st2, gmeta, 0, ngb, qi, half, right, lim);
+      for (int t0 = KT; t0 < ngb; t0 += KT) {  // more than 64 global tokens
+        gather_rows(gq, gix, t0, ngb, wave, lane);
+        gm = gix[min(t0 + lane, ngb - 1)];
         __syncthreads();  // stage 2 and gmeta are free again
         dma_gather(c.a2, kb, vb, gq, wave, lane);
-        if (tid < KT) gmeta_write(gmeta, gm, t0 + tid < p.ng, r, dil, tid);
+        if (tid < KT) gmeta_write(gmeta, gm, t0 + tid < ngb, r, dil, tid);
         wait_vmcnt<0>();
         __syncthreads();
-        if (wave_live) glob_cols_tile<T>(acc, qf, c, st2, gmeta, t0, p.ng, qi, half, right, lim);
+        if (wave_live) glob_cols_tile<T>(acc, qf, c, st2, gmeta, t0, ngb, qi, half, right, lim);
       }
       // the first ring step's barrier orders these reads of stage 2 before
       // the load of band tile 2 into it
@@ -910,23 +928,23 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
     // fp32: two ring stages; the global columns go through stage 0 first
     load_q(qf, qrow, g);
     wait_vmcnt<0>();
-    if (p.ng > 0) {
+    if (ngb > 0) {
       constexpr int NC = TileRegs<T, 256>::NC;
-      for (int t0 = 0; t0 < p.ng; t0 += KT) {
+      for (int t0 = 0; t0 < ngb; t0 += KT) {
         TileRegs<T, 256> tr;
         int gp[NC];
 #pragma unroll
-        for (int u = 0; u < NC; ++u) gp[u] = p.gidx[min(t0 + (tid + 256 * u) / CPR, p.ng - 1)];
+        for (int u = 0; u < NC; ++u) gp[u] = gix[min(t0 + (tid + 256 * u) / CPR, ngb - 1)];
 #pragma unroll
         for (int u = 0; u < NC; ++u) {
           const long off = (long)gp[u] * ROWB + ((tid + 256 * u) % CPR) * 16;
           tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
           tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
         }
-        if (tid < KT) gmeta_write(gmeta, p.gidx[min(t0 + tid, p.ng - 1)], t0 + tid < p.ng, r, dil, tid);
+        if (tid < KT) gmeta_write(gmeta, gix[min(t0 + tid, ngb - 1)], t0 + tid < ngb, r, dil, tid);
         tile_commit<T, 256>(tr, st0, st0 + TILEB, tid);
         __syncthreads();
-        if (wave_live) glob_cols_tile<T>(acc, qf, c, st0, gmeta, t0, p.ng, qi, half, right, lim);
+        if (wave_live) glob_cols_tile<T>(acc, qf, c, st0, gmeta, t0, ngb, qi, half, right, lim);
         __syncthreads();
       }
     }
@@ -965,15 +983,17 @@ DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char*
   const int grp = (gb / p.nsplit) % p.ngroup;
   const int bh = gb / (p.nsplit * p.ngroup);
   const long base = (long)bh * p.n * ROWB;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  if (gs.n <= grp * BAND_WAVES * 32) return;  // no rows of this item's set in this group
 
   const int qb = grp * BAND_WAVES + wave;  // this wave's block of 32 global rows
-  const bool live = qb < p.nqb;
+  const bool live = qb * 32 < gs.n;
   const int gi = qb * 32 + (lane & 31);
-  const int pos_q = p.gidx[min(gi, p.ng - 1)];
+  const int pos_q = gs.idx[min(gi, gs.n - 1)];
   // G is sorted: the first row of the wave and the last row of the group
   // bound the causal key ranges.
-  const int gmin = p.gidx[min(qb * 32, p.ng - 1)];
-  const int gmax = p.gidx[min(grp * BAND_WAVES * 32 + BAND_WAVES * 32 - 1, p.ng - 1)];
+  const int gmin = gs.idx[min(qb * 32, gs.n - 1)];
+  const int gmax = gs.idx[min(grp * BAND_WAVES * 32 + BAND_WAVES * 32 - 1, gs.n - 1)];
   const int k_lo = sp * p.ksplit;
   int k_hi = min(p.n, k_lo + p.ksplit);
   if (p.causal) k_hi = min(k_hi, gmax + 1);
@@ -997,7 +1017,7 @@ DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char*
 
   if (live) {
     const float ltot = pair_sum(acc.l);
-    if (gi < p.ng) {
+    if (gi < gs.n) {
       const long slot = ((long)bh * p.ng + gi) * p.nsplit + sp;
       float* po = p.part_o + slot * HD;
 #pragma unroll
@@ -1056,6 +1076,8 @@ template <class T>
 __global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
   __shared__ float sm[4][HD], sl[4][HD], sa[4][HD];
   const int gi = blockIdx.x % p.ng, bh = blockIdx.x / p.ng, tid = threadIdx.x;
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  if (gi >= gs.n) return;
   const int d = tid & 63, grp = tid >> 6;
   const long slot0 = ((long)bh * p.ng + gi) * p.nsplit;
   const float* ml = p.part_ml + slot0 * 2;
@@ -1081,7 +1103,7 @@ __global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
   if (tid < HD) {
 #pragma unroll
     for (int q = 1; q < 4; ++q) lse_fold(M, L, A, sm[q][d], sl[q][d], sa[q][d], p.c2);
-    const int pos = p.gidx[gi];
+    const int pos = gs.idx[gi];
     T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
     orow[d] = (T)(A / L);
     if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);

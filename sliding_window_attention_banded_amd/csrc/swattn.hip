@@ -50,7 +50,9 @@ struct swattn_plan {
   int nsplit, ksplit, nqb, ngroup, nglob_blocks;
   void* dev_mem;          // one allocation, carved below
   TileRec* tiles;         // [nband_blocks], NULL with the uniform decode
-  int* gidx;              // [ng]
+  int* gidx;              // [n_global]: one sorted set, or the items' sorted sets
+  int* goff;              // [B+1] offsets of the items' sets, NULL with one set
+  bool per_item;
   float* part_o;          // [B*H][ng][nsplit][64]
   float* part_ml;         // [B*H][ng][nsplit][2]
   float* bwd_lse2;        // [B*H][n] backward row statistics (bf16 plans)
@@ -93,16 +95,34 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
     if (p->dilation[h] < 1)
       return fail(SWATTN_ERR_INVALID_ARG, "dilation[" + std::to_string(h) + "] must be >= 1");
   }
-  if (p->n_global < 0 || p->n_global > p->n) return fail(SWATTN_ERR_INVALID_ARG, "n_global must be in [0, n]");
+  const bool per_item = p->global_offsets != nullptr;
+  const long gmax_total = per_item ? (long)p->batch * p->n : (long)p->n;
+  if (p->n_global < 0 || p->n_global > gmax_total)
+    return fail(SWATTN_ERR_INVALID_ARG, per_item ? "n_global must be in [0, batch*n]" : "n_global must be in [0, n]");
   if (p->n_global > 0 && !p->global_idx) return fail(SWATTN_ERR_INVALID_ARG, "global_idx must not be NULL when n_global > 0");
-  std::vector<int> G;
-  if (p->n_global > 0) {
-    G.assign(p->global_idx, p->global_idx + p->n_global);
-    for (int x : G)
-      if (x < 0 || x >= p->n) return fail(SWATTN_ERR_INVALID_ARG, "global index out of [0, n)");
-    std::sort(G.begin(), G.end());
-    if (std::adjacent_find(G.begin(), G.end()) != G.end())
-      return fail(SWATTN_ERR_INVALID_ARG, "global_idx repeats an index");
+  // G: one sorted set, or the items' sorted sets one after another (goff)
+  std::vector<int> G, goff;
+  int ng_max = p->n_global;
+  if (per_item) {
+    goff.assign(p->global_offsets, p->global_offsets + p->batch + 1);
+    if (goff[0] != 0 || goff[p->batch] != p->n_global)
+      return fail(SWATTN_ERR_INVALID_ARG, "global_offsets must start at 0 and end at n_global");
+    ng_max = 0;
+    for (int b = 0; b < p->batch; ++b) {
+      if (goff[b + 1] < goff[b]) return fail(SWATTN_ERR_INVALID_ARG, "global_offsets must not decrease");
+      if (goff[b + 1] - goff[b] > p->n) return fail(SWATTN_ERR_INVALID_ARG, "an item's global set is larger than n");
+      ng_max = std::max(ng_max, goff[b + 1] - goff[b]);
+    }
+  } else {
+    goff = {0, p->n_global};
+  }
+  if (p->n_global > 0) G.assign(p->global_idx, p->global_idx + p->n_global);
+  for (size_t b = 0; b + 1 < goff.size(); ++b) {
+    auto s0 = G.begin() + goff[b], s1 = G.begin() + goff[b + 1];
+    for (auto it = s0; it != s1; ++it)
+      if (*it < 0 || *it >= p->n) return fail(SWATTN_ERR_INVALID_ARG, "global index out of [0, n)");
+    std::sort(s0, s1);
+    if (std::adjacent_find(s0, s1) != s1) return fail(SWATTN_ERR_INVALID_ARG, "global_idx repeats an index");
   }
   if (p->d != HD) return fail(SWATTN_ERR_UNSUPPORTED, "only d = 64 is supported");
   if (p->dtype != SWATTN_BF16 && p->dtype != SWATTN_FP32) return fail(SWATTN_ERR_UNSUPPORTED, "unknown dtype");
@@ -144,7 +164,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   swattn_plan* pl = new (std::nothrow) swattn_plan();
   if (!pl) return fail(SWATTN_ERR_HIP, "host allocation failed");
   pl->B = p->batch; pl->H = p->heads; pl->n = p->n; pl->d = p->d;
-  pl->causal = p->causal; pl->ng = p->n_global; pl->dtype = p->dtype;
+  pl->causal = p->causal; pl->ng = ng_max; pl->dtype = p->dtype;
+  pl->per_item = per_item && ng_max > 0;
   pl->nband_blocks = (int)nband_blocks;
   pl->uni_half = half[0];
   pl->uni_right = p->causal ? 0 : half[0];
@@ -169,6 +190,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t sz_tiles = al(sizeof(TileRec) * std::max<size_t>(tiles.size(), 1));
   const size_t sz_g = al(sizeof(int) * std::max<size_t>(G.size(), 1));
+  const size_t sz_goff = al(sizeof(int) * goff.size());
   const size_t nslot = (size_t)bh * pl->ng * pl->nsplit;
   const size_t sz_po = al(sizeof(float) * HD * nslot);
   const size_t sz_pml = al(sizeof(float) * 2 * nslot);
@@ -193,12 +215,13 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const size_t sz_gstat = al(sizeof(float) * (size_t)bh * pl->ngp);
   const size_t sz_gkv = al(sizeof(float) * (size_t)bh * pl->nchunk * pl->ng32 * 2 * HD);
   const size_t sz_heads = al(sizeof(HeadGeom) * p->heads);
-  const size_t total = sz_tiles + sz_g + sz_po + sz_pml + 2 * sz_stat + 2 * sz_gstat + sz_gkv + sz_heads;
+  const size_t total = sz_tiles + sz_g + sz_goff + sz_po + sz_pml + 2 * sz_stat + 2 * sz_gstat + sz_gkv + sz_heads;
   e = hipMalloc(&pl->dev_mem, total);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
   char* m = static_cast<char*>(pl->dev_mem);
   pl->tiles = tiles.empty() ? nullptr : reinterpret_cast<TileRec*>(m); m += sz_tiles;
   pl->gidx = reinterpret_cast<int*>(m); m += sz_g;
+  pl->goff = pl->per_item ? reinterpret_cast<int*>(m) : nullptr; m += sz_goff;
   pl->part_o = reinterpret_cast<float*>(m); m += sz_po;
   pl->part_ml = reinterpret_cast<float*>(m); m += sz_pml;
   pl->bwd_lse2 = sz_stat ? reinterpret_cast<float*>(m) : nullptr; m += sz_stat;
@@ -210,6 +233,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   e = hipSuccess;
   if (!tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess && pl->goff) e = hipMemcpy(pl->goff, goff.data(), sizeof(int) * goff.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && bwd_g) {
     // padding rows of the global-row statistics: P = 0 and D = 0 for ever
     const std::vector<float> inf((size_t)bh * pl->ngp, std::numeric_limits<float>::infinity());
@@ -301,7 +325,7 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   const float scale = 0.125f;  // 1/sqrt(64)
   BandParams bp;
   bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.lse = lse;
-  bp.tiles = pl->tiles; bp.gidx = pl->gidx; bp.ng = pl->ng;
+  bp.tiles = pl->tiles; bp.gidx = pl->gidx; bp.goff = pl->goff; bp.ng = pl->ng;
   bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
   bp.uni_nqb = pl->uni_nqb;
   bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
@@ -309,6 +333,7 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   GlobalParams gp;
   gp.qg = qg; gp.kg = kg; gp.vg = vg; gp.o = o; gp.lse = lse; gp.gidx = pl->gidx;
   gp.part_o = pl->part_o; gp.part_ml = pl->part_ml;
+  gp.goff = pl->goff; gp.H = pl->H;
   gp.ng = pl->ng; gp.n = pl->n; gp.causal = pl->causal;
   gp.nsplit = pl->nsplit; gp.ksplit = pl->ksplit; gp.nqb = pl->nqb; gp.ngroup = pl->ngroup;
   gp.c2 = scale * LOG2E; gp.scale = scale;
@@ -409,7 +434,7 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   bp.tiles = pl->tiles; bp.heads = pl->bwd_heads;
   bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
   bp.uni_nqb = pl->uni_nqb;
-  bp.gidx = pl->gidx; bp.ng = pl->ng; bp.ngp = pl->ngp; bp.ng32 = pl->ng32;
+  bp.gidx = pl->gidx; bp.goff = pl->goff; bp.ng = pl->ng; bp.ngp = pl->ngp; bp.ng32 = pl->ng32;
   bp.n = pl->n; bp.H = pl->H; bp.causal = pl->causal;
   bp.nsplit = pl->nsplit; bp.ksplit = pl->ksplit; bp.nqb = pl->nqb; bp.ngroup = pl->ngroup;
   bp.nchunk = pl->nchunk; bp.nkgb = pl->nkgb;

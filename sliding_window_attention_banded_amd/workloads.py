@@ -18,7 +18,8 @@ from dataclasses import dataclass, field, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "DTYPES"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "DTYPES", "item_globals", "has_globals",
+           "global_union"]
 
 DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
@@ -33,6 +34,8 @@ class Workload:
     window: tuple
     dilation: tuple
     causal: bool
+    # one set of global positions for every batch item, or (per-example
+    # global tokens) a tuple of B such sets
     global_idx: tuple = field(default=())
     dtype: str = "bf16"
     scale: float = 0.125
@@ -43,6 +46,24 @@ class Workload:
 
     def with_(self, **kw):
         return replace(self, **kw)
+
+
+def item_globals(wl):
+    """The global positions of each batch item (a list of B tuples)."""
+    g = tuple(wl.global_idx)
+    if g and all(isinstance(x, (tuple, list)) for x in g):
+        if len(g) != wl.batch:
+            raise ValueError("per-example global_idx needs one set per batch item")
+        return [tuple(x) for x in g]
+    return [g] * wl.batch
+
+
+def has_globals(wl):
+    return any(len(x) for x in item_globals(wl))
+
+
+def global_union(wl):
+    return sorted(set(x for g in item_globals(wl) for x in g))
 
 
 def _per_head(h, v, over=None):
@@ -78,6 +99,11 @@ WORKLOADS = {
     "qa_b4_h12_n4096_w512_g64": Workload(
         "qa_b4_h12_n4096_w512_g64", 4, 12, 4096, 64, _per_head(12, 512),
         _per_head(12, 1), False, tuple(range(64))),
+    # QA-style with per-example questions: item b's first L_b tokens are its
+    # global tokens, L = (64, 48, 24, 96)
+    "qa_b4_h12_n4096_w512_gper": Workload(
+        "qa_b4_h12_n4096_w512_gper", 4, 12, 4096, 64, _per_head(12, 512),
+        _per_head(12, 1), False, tuple(tuple(range(L)) for L in (64, 48, 24, 96))),
     # LED encoder: 16K tokens, window 1024, global attention on the first token
     "led_b1_h12_n16384_w1024_g1": Workload(
         "led_b1_h12_n16384_w1024_g1", 1, 12, 16384, 64, _per_head(12, 1024),
@@ -107,7 +133,8 @@ def make_inputs(wl: Workload, seed: int, kind: str = "normal"):
       * "sharp":  q, k ~ N(0,1) * 2 and v ~ U(-1, 1), so softmax rows are
         peaked and a wrong key set moves the output far beyond tolerance;
       * "dedup":  "normal", plus a direction u shared by every query and by the
-        regular keys at up to four global positions (every len(G)//4-th), with
+        regular keys at up to four global positions (every len(G)//4-th of
+        the union of the items' sets), with
         one-hot values at those positions: each such key then takes a large
         share of every row, so counting it twice (when it also lies inside a
         row's window) moves the output far beyond tolerance.
@@ -117,15 +144,16 @@ def make_inputs(wl: Workload, seed: int, kind: str = "normal"):
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     shape = (wl.batch, wl.heads, wl.n, wl.d)
     out = {}
-    roles = ["q", "k", "v"] + (["qg", "kg", "vg"] if wl.global_idx else [])
+    roles = ["q", "k", "v"] + (["qg", "kg", "vg"] if has_globals(wl) else [])
     for r in roles:
         out[r] = _draw(gen, shape, wl.scale, kind,
                        "v" if r in ("v", "vg") else "qk")
-    if kind == "dedup" and wl.global_idx:
+    if kind == "dedup" and has_globals(wl):
         u = torch.randn((wl.d,), generator=gen, dtype=torch.float32)
         u = u / u.norm() * wl.d ** 0.5
-        step = max(1, len(wl.global_idx) // 4)
-        gi = torch.tensor(sorted(wl.global_idx)[::step], dtype=torch.long)
+        gu = global_union(wl)
+        step = max(1, len(gu) // 4)
+        gi = torch.tensor(gu[::step], dtype=torch.long)
         out["q"] = out["q"] + 0.25 * u
         out["k"][:, :, gi, :] = 3.0 * u
         vv = torch.zeros((len(gi), wl.d), dtype=torch.float32)

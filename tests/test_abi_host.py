@@ -35,11 +35,14 @@ def _params(**kw):
     dil = (ctypes.c_int32 * heads)(*kw.get("dilation", [1] * heads))
     gl = kw.get("global_idx", [])
     G = (ctypes.c_int32 * max(1, len(gl)))(*gl)
+    offs = kw.get("offsets")
+    O = (ctypes.c_int32 * len(offs))(*offs) if offs is not None else None
     p = binding._Params(kw.get("batch", 1), heads, kw.get("n", 16), kw.get("d", 64),
                         win, dil, kw.get("causal", 0),
                         ctypes.cast(G, ctypes.POINTER(ctypes.c_int32)),
-                        kw.get("n_global", len(gl)), kw.get("dtype", 0))
-    return p, (win, dil, G)
+                        kw.get("n_global", len(gl)), kw.get("dtype", 0),
+                        ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O is not None else None)
+    return p, (win, dil, G, O)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -49,6 +52,14 @@ def _params(**kw):
     (dict(global_idx=[3, 3]), 1), (dict(global_idx=[16]), 1),
     (dict(global_idx=[-1]), 1), (dict(n_global=17), 1), (dict(d=128), 2),
     (dict(dtype=7), 2),
+    # per-example sets: offsets must start at 0, end at n_global, not decrease;
+    # each item's set in [0, n), no repeats within an item, at most n entries
+    (dict(batch=2, global_idx=[1, 2], offsets=[1, 1, 2]), 1),
+    (dict(batch=2, global_idx=[1, 2], offsets=[0, 1, 3], n_global=2), 1),
+    (dict(batch=2, global_idx=[1, 2], offsets=[0, 2, 1], n_global=2), 1),
+    (dict(batch=2, global_idx=[1, 1], offsets=[0, 2, 2]), 1),
+    (dict(batch=2, global_idx=[1, 16], offsets=[0, 1, 2]), 1),
+    (dict(batch=2, n=2, global_idx=[0, 1, 1], offsets=[0, 3, 3]), 1),
 ])
 def test_create_rejects_bad_parameters(lib, kw, code):
     p, keep = _params(**kw)

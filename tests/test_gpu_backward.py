@@ -22,7 +22,8 @@ import numpy as np
 import pytest
 import torch
 
-from sliding_window_attention_banded_amd.workloads import WORKLOADS, Workload, make_inputs
+from sliding_window_attention_banded_amd.workloads import (
+    WORKLOADS, Workload, item_globals, make_inputs)
 from tests._lib import ensure_library, to64
 
 pytestmark = pytest.mark.gpu
@@ -55,6 +56,8 @@ SMALL = [
     W("b_g_causal", 1, 4, 500, (32, 256, 2, 1024), (1, 4, 1, 2), True, (5, 250, 499)),
     W("b_g_many", 1, 2, 700, (64, 16), (1, 3), False, tuple(range(0, 700, 7))),
     W("b_g_all", 1, 2, 130, (8, 4), (1, 2), False, tuple(range(130))),
+    W("b_per_item", 3, 2, 500, (64, 16), (1, 3), False, ((0, 5, 499), (), tuple(range(100, 190)))),
+    W("b_per_item_causal", 2, 3, 400, (32, 256, 2), (1, 4, 1), True, ((7,), (0, 250, 399))),
 ]
 
 GRADS = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
@@ -90,7 +93,7 @@ def _oracle_grads(wl, inp, dout, bh=None):
     for b, h in bh:
         sl = [None if x is None else x[b:b + 1, h:h + 1] for x in t]
         outs.append(attention_backward(*sl, window=win[h], dilation=dil[h], causal=wl.causal,
-                                       global_idx=list(wl.global_idx)))
+                                       global_idx=list(item_globals(wl)[b])))
     return outs
 
 
@@ -128,6 +131,7 @@ def test_backward_small(wl, kind):
     ("encoder_b2_h12_n4096_w512_g1", [(0, 5), (1, 0)]),
     ("arlm_b1_h12_n8192_w512_causal_dil2", [(0, 3), (0, 11)]),
     ("qa_b4_h12_n4096_w512_g64", [(3, 7)]),
+    ("qa_b4_h12_n4096_w512_gper", [(2, 1), (3, 5)]),
 ])
 @pytest.mark.parametrize("kind", ["normal", "sharp"])
 def test_backward_full_size_slices(name, bh, kind):

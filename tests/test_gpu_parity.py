@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from sliding_window_attention_banded_amd.workloads import WORKLOADS, Workload, make_inputs
+from sliding_window_attention_banded_amd.workloads import (
+    WORKLOADS, Workload, global_union, has_globals, make_inputs)
 from tests._lib import compare, ensure_library, oracle_ref, run_gpu
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +41,10 @@ SMALL = [
     W("dil_beyond_n", 1, 2, 150, (8, 4), (200, 149), False),
     W("all_global", 1, 2, 130, (8, 4), (1, 2), False, tuple(range(130))),
     W("all_global_causal", 1, 1, 130, 8, 1, True, tuple(range(130))),
+    # one set of global tokens per batch item (one item with none, one with
+    # more than a 64-key tile)
+    W("per_item", 3, 2, 700, (64, 16), (1, 3), False, ((0, 5, 699), (), tuple(range(100, 190)))),
+    W("per_item_causal", 2, 3, 500, (32, 256, 2), (1, 4, 1), True, ((7,), (0, 250, 499))),
 ]
 
 EDGE_N = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255]
@@ -61,7 +66,7 @@ def test_small_full_compare(wl, kind):
         _case(wl, seed, kind)
 
 
-@pytest.mark.parametrize("wl", [w for w in SMALL if w.global_idx], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [w for w in SMALL if has_globals(w)], ids=lambda w: w.name)
 def test_small_dedup(wl):
     _case(wl, 0, "dedup")
 
@@ -82,21 +87,22 @@ def _sample_rows(wl, count=48, seed=0):
              511, 512, 513, n // 2, n - 300, n - 257, n - 256, n - 129, n - 128,
              n - 65, n - 64, n - 33, n - 32, n - 2, n - 1]
     rows = set(r for r in fixed if 0 <= r < n)
-    rows |= set(int(x) for x in wl.global_idx[:4]) | set(int(x) for x in wl.global_idx[-2:])
+    gu = global_union(wl)
+    rows |= set(int(x) for x in gu[:4]) | set(int(x) for x in gu[-2:])
     rows |= set(int(x) for x in rng.integers(0, n, count))
     return np.array(sorted(rows))
 
 
 FULL = ["encoder_b2_h12_n4096_w512_g1", "encoder_b2_h12_n4096_w512",
         "arlm_b1_h12_n8192_w512_causal_dil2", "arlm_b1_h8_n23040_w1024_causal_dil4",
-        "qa_b4_h12_n4096_w512_g64", "led_b1_h12_n16384_w1024_g1"]
+        "qa_b4_h12_n4096_w512_g64", "qa_b4_h12_n4096_w512_gper", "led_b1_h12_n16384_w1024_g1"]
 
 
 @pytest.mark.parametrize("name", FULL)
 @pytest.mark.parametrize("kind", ["normal", "sharp", "dedup"])
 def test_full_size_sampled_rows(name, kind):
     wl = WORKLOADS[name]
-    if kind == "dedup" and not wl.global_idx:
+    if kind == "dedup" and not has_globals(wl):
         pytest.skip("dedup inputs need global tokens")
     _case(wl, 0, kind, rows=_sample_rows(wl))
 
