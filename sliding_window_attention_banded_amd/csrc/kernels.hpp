@@ -1079,6 +1079,7 @@ __global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
   if (gi >= gs.n) return;
   const int d = tid & 63, grp = tid >> 6;
+  const int pos = gs.idx[gi];  // loaded with the partials, not after them
   const long slot0 = ((long)bh * p.ng + gi) * p.nsplit;
   const float* ml = p.part_ml + slot0 * 2;
   const float* po = p.part_o + slot0 * HD + d;
@@ -1103,7 +1104,6 @@ __global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
   if (tid < HD) {
 #pragma unroll
     for (int q = 1; q < 4; ++q) lse_fold(M, L, A, sm[q][d], sl[q][d], sa[q][d], p.c2);
-    const int pos = gs.idx[gi];
     T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
     orow[d] = (T)(A / L);
     if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
