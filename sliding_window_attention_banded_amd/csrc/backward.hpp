@@ -489,7 +489,17 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
 
 // ----------------------------------------------------------------------------
 // Global rows: dQg partials (query blocks over chunks of Kg, Vg, as in the
-// forward's global-row blocks).
+// forward's global-row blocks). When the block holds fewer than four
+// 32-row groups of G, the waves of a group split its 32-key units and their
+// partials are summed in LDS.
+
+struct GlobPolSplit {
+  GlobPol base;
+  int kbeg, sub, wpg;
+  DEV bool active(int ku) const { return base.active(ku) && ((ku - kbeg) >> 5) % wpg == sub; }
+  DEV bool interior(int ku) const { return base.interior(ku); }
+  template <class T> DEV void mask(f32x16& s, int ku, int g) const { base.template mask<T>(s, ku, g); }
+};
 
 DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st2) {
   constexpr int ROWB = ElemTraits<__bf16>::ROWB;
@@ -502,8 +512,11 @@ DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st
   const long base = (long)bh * p.n * ROWB;
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
   if (gs.n <= grp * BAND_WAVES * 32) return;  // no rows of this item's set in this group
-  const int qb = grp * BAND_WAVES + wave;
-  const bool live = qb * 32 < gs.n;
+  const int qfrags = min(BAND_WAVES, (gs.n + 31) / 32 - grp * BAND_WAVES);
+  const int wpg = BAND_WAVES / qfrags;
+  const int qbl = wave / wpg, sub = wave % wpg;
+  const int qb = grp * BAND_WAVES + qbl;
+  const bool live = qbl < qfrags;
   const int gi = qb * 32 + (lane & 31);
   const int pos_q = gs.idx[min(gi, gs.n - 1)];
   const int gmin = gs.idx[min(qb * 32, gs.n - 1)];
@@ -518,7 +531,7 @@ DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st
             reinterpret_cast<const char*>(p.kg) + base, reinterpret_cast<const char*>(p.vg) + base,
             k_lo, k_hi, nband, 0, 1, wave, lane, g, live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
-  const GlobPol pol{p.causal ? pos_q : 0x7fffffff - 1, k_hi, gmin, p.causal};
+  const GlobPolSplit pol{{p.causal ? pos_q : 0x7fffffff - 1, k_hi, gmin, p.causal}, k_lo, sub, wpg};
   DqWave w;
   acc2_zero(w.dq);
   if (nband > 0) {
@@ -538,23 +551,38 @@ DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st
     }
     wait_vmcnt<0>();
   }
-  if (live && gi < gs.n) {
-    float* po = p.part_dqg + (((long)bh * p.ng + gi) * p.nsplit + sp) * HD;
+  // sum the waves of each row group in LDS, one partial per global row
+  __syncthreads();  // the stages are free
+  float* W = reinterpret_cast<float*>(wave < 2 ? st0 : st1) + (wave & 1) * 32 * HD;  // [32][64]
 #pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
+  for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        f32x4 t;
+    for (int a = 0; a < 4; ++a) {
+      f32x4 t;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = w.dq.a[dh][4 * a + e];
-        *reinterpret_cast<f32x4*>(po + 32 * dh + 8 * a + 4 * g) = t;
-      }
+      for (int e = 0; e < 4; ++e) t[e] = w.dq.a[dh][4 * a + e];
+      *reinterpret_cast<f32x4*>(W + (lane & 31) * HD + 32 * dh + 8 * a + 4 * g) = t;
+    }
+  __syncthreads();
+  for (int idx = tid; idx < qfrags * 32 * HD; idx += 256) {
+    const int qf = idx / (32 * HD), r = (idx / HD) % 32, d = idx % HD;
+    const int row = (grp * BAND_WAVES + qf) * 32 + r;
+    if (row >= gs.n) continue;
+    float acc = 0.f;
+    for (int sw = 0; sw < wpg; ++sw) {
+      const int wv = qf * wpg + sw;
+      acc += reinterpret_cast<const float*>(wv < 2 ? st0 : st1)[(wv & 1) * 32 * HD + r * HD + d];
+    }
+    p.part_dqg[(((long)bh * p.ng + row) * p.nsplit + sp) * HD + d] = acc;
   }
 }
 
 // ----------------------------------------------------------------------------
-// Global rows: dKg, dVg (key blocks over 128 positions of Kg, Vg; the query
-// tiles are the rows of G, gathered from Qg and dO).
+// Global rows: dKg, dVg (key blocks over GKV_GROUPS x 128 positions of Kg,
+// Vg, one 128-position group after another; the query tiles are the rows of
+// G gathered from Qg and dO, loaded once when there are at most 64).
+
+constexpr int GKV_GROUPS = 4;
 
 DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
   constexpr int ROWB = ElemTraits<__bf16>::ROWB;
@@ -562,56 +590,68 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nkb = (p.n + BM - 1) / BM;
+  const int span = BM * GKV_GROUPS;
+  const int nkb = (p.n + span - 1) / span;
   const int bh = blk / nkb;
-  const int k0 = (blk - bh * nkb) * BM;
+  const int kbase = (blk - bh * nkb) * span;
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
   const int ngb = gs.n;
   const long base = (long)bh * p.n * ROWB;
-  const int kw0 = k0 + 32 * wave;
-  const bool wave_live = kw0 < p.n;
-  const int kj = kw0 + (lane & 31);
-  const bool key_ok = kj < p.n;
-  const int pos_k = min(kj, p.n - 1);
-  const long roff = base + (long)pos_k * ROWB;
   LdsLanes ll;
   lds_lanes_init(ll, lane);
   const unsigned a0 = (unsigned)(uintptr_t)(lds_void*)st0;
   const char* qb = reinterpret_cast<const char*>(p.qg) + base;
   const char* db = reinterpret_cast<const char*>(p.dout) + base;
 
-  DkvWave w;
-  acc2_zero(w.dk);
-  acc2_zero(w.dv);
-  load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.kg) + roff), g);
-  load_q(w.vf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.vg) + roff), g);
-  for (int t0 = 0; t0 < ngb; t0 += KT) {
+  // gather global rows t0 .. t0+63 with their statistics into stage 0
+  auto load_tile = [&](int t0, bool first) {
     int gq[4];
     gather_rows(gq, gs.idx, t0, ngb, wave, lane);
     const int gp = gs.idx[min(t0 + lane, ngb - 1)];
-    if (t0 > 0) __syncthreads();  // the previous tile is consumed
+    if (!first) __syncthreads();  // the previous tile is consumed
     dma_gather(a0, qb, db, gq, wave, lane);
     const float* src = ((wave & 1) ? p.gdd : p.glse2) + (long)bh * p.ngp + t0 + lane;
     dma4(src, a0 + (unsigned)(2 * TILEB + 256 * wave));
     if (tid < KT) gpos[tid] = gp;
     wait_vmcnt<0>();
     __syncthreads();
-    if (wave_live) {
+  };
+  const bool one_tile = ngb <= KT;
+  if (one_tile && ngb > 0) load_tile(0, true);
+
+  for (int it = 0; it < GKV_GROUPS; ++it) {
+    const int k0 = kbase + it * BM;
+    if (k0 >= p.n) break;  // workgroup-uniform
+    const int kw0 = k0 + 32 * wave;
+    const bool wave_live = kw0 < p.n;
+    const int kj = kw0 + (lane & 31);
+    const bool key_ok = kj < p.n;
+    const int pos_k = min(kj, p.n - 1);
+    const long roff = base + (long)pos_k * ROWB;
+    DkvWave w;
+    acc2_zero(w.dk);
+    acc2_zero(w.dv);
+    load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.kg) + roff), g);
+    load_q(w.vf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.vg) + roff), g);
+    for (int t0 = 0; t0 < ngb; t0 += KT) {
+      if (!one_tile) load_tile(t0, it == 0 && t0 == 0);
+      if (wave_live) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        if (t0 + 32 * kh >= ngb) continue;
-        dkv_unit(w, st0, kh, ll, p.c2, g, p.causal != 0, [&](f32x16& t) {
-          // causal: key position <= the global row's position
+        for (int kh = 0; kh < 2; ++kh) {
+          if (t0 + 32 * kh >= ngb) continue;
+          dkv_unit(w, st0, kh, ll, p.c2, g, p.causal != 0, [&](f32x16& t) {
+            // causal: key position <= the global row's position
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (pos_k > gpos[32 * kh + key_of_reg<__bf16>(j, g)]) t[j] = -__builtin_inff();
-        });
+            for (int j = 0; j < 16; ++j)
+              if (pos_k > gpos[32 * kh + key_of_reg<__bf16>(j, g)]) t[j] = -__builtin_inff();
+          });
+        }
       }
     }
-  }
-  if (wave_live && key_ok) {
-    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dkg) + roff), w.dk, p.scale, g);
-    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dvg) + roff), w.dv, 1.0f, g);
+    if (wave_live && key_ok) {
+      store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dkg) + roff), w.dk, p.scale, g);
+      store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dvg) + roff), w.dv, 1.0f, g);
+    }
   }
 }
 
@@ -741,18 +781,28 @@ __global__ __launch_bounds__(256) void bwd_gred(BwdParams p) {
   if (gi >= gs.n) return;
   const int t = threadIdx.x, d = t & 63, part = t >> 6;
   const long row = bh * p.n + gs.idx[gi];
-  if (part == 0) {
-    const float* src = p.part_dqg + ((bh * p.ng + gi) * p.nsplit) * HD + d;
+  // sum `count` partials `stride` floats apart, eight loads in flight at once
+  auto sum = [](const float* src, int count, long stride) {
     float acc = 0.f;
-    for (int sp = 0; sp < p.nsplit; ++sp) acc += src[(long)sp * HD];
+    for (int c0 = 0; c0 < count; c0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = c0 + i < count ? src[(c0 + i) * stride] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += x[i];
+    }
+    return acc;
+  };
+  if (part == 0) {
+    const float acc = sum(p.part_dqg + ((bh * p.ng + gi) * p.nsplit) * HD + d, p.nsplit, HD);
     reinterpret_cast<__bf16*>(p.dqg)[row * HD + d] = (__bf16)(acc * p.scale);
   } else if (part <= 2) {
     const int off = part == 1 ? 0 : HD;
-    const float* src = p.part_gkv + ((bh * p.nchunk) * p.ng32 + gi) * (2 * HD) + off + d;
-    float acc = 0.f;
-    for (int ch = 0; ch < p.nchunk; ++ch) acc += src[(long)ch * p.ng32 * 2 * HD];
     __bf16* dst = reinterpret_cast<__bf16*>(part == 1 ? p.dk : p.dv) + row * HD + d;
-    *dst = (__bf16)((float)*dst + (part == 1 ? acc * p.scale : acc));
+    const float band = (float)*dst;
+    const float acc = sum(p.part_gkv + ((bh * p.nchunk) * p.ng32 + gi) * (2 * HD) + off + d,
+                          p.nchunk, (long)p.ng32 * 2 * HD);
+    *dst = (__bf16)(band + (part == 1 ? acc * p.scale : acc));
   }
 }
 

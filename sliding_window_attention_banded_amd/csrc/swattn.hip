@@ -202,7 +202,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->nchunk = bwd_g ? (p->n + GCOL_QC - 1) / GCOL_QC : 0;
   pl->nkgb = bwd_g ? ((pl->ng + 31) / 32 + BAND_WAVES - 1) / BAND_WAVES : 0;
   {
-    const long n_gkv = bwd_g ? bh * ((p->n + BM - 1) / BM) : 0;
+    const long n_gkv = bwd_g ? bh * ((p->n + BM * GKV_GROUPS - 1) / (BM * GKV_GROUPS)) : 0;
     const long n_gcol = bwd_g ? bh * (long)pl->nchunk * pl->nkgb : 0;
     const long nbwd = 2 * nband_blocks + (bwd_g ? (long)pl->nglob_blocks : 0) + n_gkv + n_gcol;
     if (nbwd > 0x7fffffffL) {
