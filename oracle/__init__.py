@@ -22,3 +22,4 @@ from .masked_softmax import (  # noqa: F401
     band_mask,
     global_row_mask,
 )
+from .projection import project  # noqa: F401
