@@ -8,12 +8,13 @@ projections of the layer input, and uses a second, separate set of
 projections Qg, Kg, Vg for global attention. For input rows x (one per token,
 d_model features) and head h, projection p of head h is
 
-    P[b, h, i, :] = x[b, i, :] @ W[:, (p * H + h) * 64 : (p * H + h + 1) * 64]
-                    + bias[(p * H + h) * 64 : ...]
+    P[b, h, i, e] = sum_c x[b, i, c] * W[(p * H + h) * 64 + e, c]
+                    + bias[(p * H + h) * 64 + e]
 
-with the projections in the order q, k, v (then qg, kg, vg when global
-tokens are used). The scale 1/sqrt(64) is not folded in (the attention
-applies it).
+with W stored one output feature per row (the layout of a linear layer's
+weight, out_features x in_features) and the projections in the order q, k, v
+(then qg, kg, vg when global tokens are used). The scale 1/sqrt(64) is not
+folded in (the attention applies it).
 """
 
 from __future__ import annotations
@@ -24,15 +25,15 @@ __all__ = ["project"]
 
 
 def project(x, w, bias, heads):
-    """x [B, n, D], w [D, P*heads*64], bias [P*heads*64] or None ->
+    """x [B, n, D], w [P*heads*64, D], bias [P*heads*64] or None ->
     list of P arrays [B, heads, n, 64], float64."""
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     B, n, D = x.shape
-    if w.shape[0] != D or w.shape[1] % (heads * 64):
-        raise ValueError("w must be [d_model, P*heads*64]")
-    P = w.shape[1] // (heads * 64)
-    y = x.reshape(B * n, D) @ w
+    if w.ndim != 2 or w.shape[1] != D or w.shape[0] % (heads * 64) or w.shape[0] == 0:
+        raise ValueError("w must be [P*heads*64, d_model]")
+    P = w.shape[0] // (heads * 64)
+    y = x.reshape(B * n, D) @ w.T
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
     y = y.reshape(B, n, P, heads, 64)
