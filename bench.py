@@ -100,6 +100,8 @@ def main():
                     help="skip the per-kernel event pass (e.g. under a profiler)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement")
+    ap.add_argument("--no-projection", action="store_true",
+                    help="skip the projection-prologue measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -251,6 +253,43 @@ def main():
                "warm": {"ms_per_step": bms_warm, "tflops": bf_b / (bms_warm * 1e-3) / 1e12},
                "tokens_per_s": tokens / (bms * 1e-3)}
 
+    proj = None
+    if not args.no_projection and wl.dtype == "bf16":
+        # the projections in front of the attention for this workload: x of
+        # d_model = heads*64 features per token into Q, K, V (and Qg, Kg, Vg
+        # with global tokens), bias included; outputs rotate over 4 buffers
+        from sliding_window_attention_banded_amd import project
+        from sliding_window_attention_banded_amd.workloads import make_projection_inputs
+        P = 6 if has_globals(wl) else 3
+        D = wl.heads * wl.d
+        px, pw, pb = (t.to(dev) for t in make_projection_inputs(wl.batch, wl.n, D, wl.heads, P, 0))
+        pouts = [torch.empty((P, wl.batch, wl.heads, wl.n, 64), dtype=torch.bfloat16, device=dev)
+                 for _ in range(4)]
+
+        def ptimed(k):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(k):
+                project(px, pw, pb, heads=wl.heads, out=pouts[i % 4], stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / k
+
+        ptimed(args.warmup)
+        pms = ptimed(args.steps)
+        M, N = wl.batch * wl.n, P * wl.heads * 64
+        pfl = 2.0 * M * N * D
+        pby = 2.0 * (M * D + N * D + N + M * N)
+        ptf = pfl / (pms * 1e-3) / 1e12
+        print(f"[bench] projection {pms * 1e3:.2f} us ({ptf:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+        proj = {"kernel": "proj_gemm", "ms_per_step": pms, "d_model": D, "projections": P,
+                "algorithmic_gflop": pfl / 1e9, "algorithmic_bytes": pby,
+                "tflops": ptf, "mfma_frac": ptf / PEAK_BF16_TFLOPS,
+                "gbs": pby / (pms * 1e-3) / 1e9, "hbm_frac": pby / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "bound": "mfma" if pfl / (PEAK_BF16_TFLOPS * 1e12) >= pby / (PEAK_HBM_GBS * 1e9) else "hbm"}
+
     line = {
         "metric": METRIC,
         "value": bf / (ms * 1e-3) / 1e12,
@@ -272,6 +311,7 @@ def main():
         "input_sets": nsets,
         "roofline": roof,
         "backward": bwd,
+        "projection": proj,
         "cpu_baseline": None,
     }
     plan.close()

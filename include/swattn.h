@@ -131,6 +131,35 @@ int swattn_backward(swattn_plan* plan, const void* q, const void* k, const void*
                     void* dqg, void* dkg, void* dvg, void* stream);
 
 /*
+ * Enqueue the projections in front of the attention on `stream` (a
+ * hipStream_t; NULL = the default stream): the linear maps that produce Q, K,
+ * V from a layer's input and, for global tokens, the separate Qg, Kg, Vg
+ * (section 3-1 of the Longformer summary page, "Linear Projections for Global
+ * Attention"). Needs no plan. For projection p < nproj, head h, token i of
+ * batch item b and feature e < 64:
+ *   out[p][b][h][i][e] = sum_c x[b][i][c] * w[(p*heads + h)*64 + e][c]
+ *                        + bias[(p*heads + h)*64 + e]
+ * accumulated in fp32, rounded once to bf16.
+ *   x     device bf16 [batch, n, d_model] contiguous;
+ *   w     device bf16 [nproj*heads*64, d_model]: one output feature per row,
+ *         the layout of a linear layer's weight; the rows of projection p
+ *         are the block p*heads*64 .. (p+1)*heads*64-1, head-major;
+ *   bias  device bf16 [nproj*heads*64] or NULL (no bias);
+ *   out   device bf16 [nproj, batch, heads, n, 64], written in full: out + p*
+ *         batch*heads*n*64 elements is projection p in the [B, H, n, d]
+ *         layout swattn_forward reads (order q, k, v, then qg, kg, vg);
+ *         must not overlap an input.
+ * d_model must be a multiple of 32 and x, w each smaller than 2 GiB; every
+ * device pointer 16-byte aligned. The caller owns every buffer; nothing is
+ * allocated. Errors: INVALID_ARG (NULL pointer, size < 1, out overlapping an
+ * input), UNSUPPORTED (dtype other than SWATTN_BF16, d_model, sizes),
+ * ALIGNMENT, HIP (launch failure).
+ */
+int swattn_project(const void* x, const void* w, const void* bias, void* out,
+                   int batch, int n, int d_model, int heads, int nproj, int dtype,
+                   void* stream);
+
+/*
  * Free the plan and its device memory. NULL is a no-op. The caller must make
  * sure no enqueued forward still uses the plan (e.g. synchronise its stream).
  */

@@ -13,12 +13,12 @@ import os
 
 import torch
 
-__all__ = ["Plan", "SwattnError", "library_path", "load_library", "EXPORTS"]
+__all__ = ["Plan", "SwattnError", "project", "library_path", "load_library", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIGNMENT = range(5)
 BF16, FP32 = 0, 1
-EXPORTS = ("swattn_create", "swattn_forward", "swattn_backward", "swattn_destroy",
+EXPORTS = ("swattn_create", "swattn_forward", "swattn_backward", "swattn_project", "swattn_destroy",
            "swattn_set_timing", "swattn_kernel_times",
            "swattn_status_string", "swattn_last_error")
 
@@ -64,6 +64,8 @@ def load_library():
     lib.swattn_forward.restype = ctypes.c_int
     lib.swattn_backward.argtypes = [vp] * 17
     lib.swattn_backward.restype = ctypes.c_int
+    lib.swattn_project.argtypes = [vp] * 4 + [ctypes.c_int] * 6 + [vp]
+    lib.swattn_project.restype = ctypes.c_int
     lib.swattn_destroy.argtypes = [vp]
     lib.swattn_destroy.restype = ctypes.c_int
     lib.swattn_set_timing.argtypes = [vp, ctypes.c_int]
@@ -227,3 +229,38 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def project(x, weight, bias=None, heads=None, out=None, stream=None):
+    """Enqueue the projections in front of the attention (swattn_project):
+    x [B, n, d_model] bf16, weight [P*heads*64, d_model] bf16 (a linear
+    layer's layout), bias [P*heads*64] bf16 or None. Returns out
+    [P, B, heads, n, 64]; out[p] is projection p (q, k, v, then qg, kg, vg)
+    in the layout Plan.forward takes."""
+    lib = load_library()
+    if heads is None or heads < 1:
+        raise SwattnError(ERR_INVALID_ARG, "heads must be given and >= 1")
+    for name, t in (("x", x), ("weight", weight), ("bias", bias)):
+        if t is None and name == "bias":
+            continue
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise SwattnError(ERR_INVALID_ARG, f"{name} must be a contiguous bf16 device tensor")
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[1] != x.shape[2] \
+            or weight.shape[0] % (heads * 64) or weight.shape[0] == 0:
+        raise SwattnError(ERR_INVALID_ARG, "need x [B, n, D] and weight [P*heads*64, D]")
+    B, n, D = x.shape
+    P = weight.shape[0] // (heads * 64)
+    if bias is not None and tuple(bias.shape) != (P * heads * 64,):
+        raise SwattnError(ERR_INVALID_ARG, "bias must be [P*heads*64]")
+    shape = (P, B, heads, n, 64)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise SwattnError(ERR_INVALID_ARG, f"out must be contiguous bf16 of shape {shape}")
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    _check(lib, lib.swattn_project(x.data_ptr(), weight.data_ptr(),
+                                   bias.data_ptr() if bias is not None else None,
+                                   out.data_ptr(), B, n, D, heads, P, BF16,
+                                   ctypes.c_void_p(st.cuda_stream)),
+           "swattn_project")
+    return out

@@ -15,7 +15,9 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libswattn.so")
 SOURCES = [os.path.join(HERE, "csrc", "swattn.hip")]
 HEADERS = [os.path.join(ROOT, "include", "swattn.h"),
-           os.path.join(HERE, "csrc", "kernels.hpp")]
+           os.path.join(HERE, "csrc", "kernels.hpp"),
+           os.path.join(HERE, "csrc", "backward.hpp"),
+           os.path.join(HERE, "csrc", "project.hpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,240 @@
+// Projection prologue: the linear projections that turn a layer's input into
+// the attention's Q, K, V and, when global tokens are used, the separate
+// Qg, Kg, Vg (Longformer summary page, section 3-1, "Linear Projections for
+// Global Attention").
+//
+// For x [M = B*n, D] and a weight W [N = P*H*64, D] (one output feature per
+// row, as a linear layer stores it) the kernel forms C^T = W x^T on the
+// matrix cores and writes each 64-feature block of C (projection p, head h)
+// straight into out[p][b][h][i][0..63], the layout the attention reads, with
+// an optional bias added in fp32 before the bf16 rounding.
+//
+// Workgroup tile: 256 tokens x 128 features, 4 waves as 2 x 2, each wave
+// 128 tokens x 64 features = 4 x 2 MFMA 32x32x16 tiles. Both operands are
+// read k-contiguous (W rows and x rows), 32 input features per stage,
+// through a 3-stage LDS ring (72 KB) filled by direct global->LDS loads, so
+// that two workgroups share a CU and one's ring fill and stores run under
+// the other's MFMAs.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace swattn {
+
+constexpr int PJ_TM = 256;                                 // tokens per workgroup
+constexpr int PJ_TN = 128;                                 // output features per workgroup
+constexpr int PJ_TK = 32;                                  // input features per stage
+constexpr int PJ_ROWB = PJ_TK * 2;                         // bytes per staged row (bf16)
+constexpr int PJ_A_BYTES = PJ_TN * PJ_ROWB;                // W tile, 8 KB
+constexpr int PJ_STAGE_BYTES = PJ_A_BYTES + PJ_TM * PJ_ROWB;  // + x tile, 24 KB
+constexpr int PJ_NI = PJ_STAGE_BYTES / 1024;               // 1-KB loads per stage
+constexpr int PJ_PER_WAVE = PJ_NI / 4;                     // 6 per wave
+constexpr int PJ_A_NI = PJ_A_BYTES / 1024;                 // the first 8 fill the W tile
+constexpr int PJ_RPB = 1024 / PJ_ROWB;                     // rows per 1-KB load
+constexpr int PJ_GROUP = 4;                                // token tiles swept together
+
+struct ProjParams {
+  const __bf16* x;     // [M][D]
+  const __bf16* w;     // [N][D]
+  const __bf16* bias;  // [N] or NULL
+  __bf16* out;         // [P][B][H][n][64]
+  int M;               // B * n
+  int N;               // P * H * 64
+  int D;               // multiple of 32
+  int n;
+  int B;
+  int H;
+  int ntm;             // ceil(M / 256)
+  int ntn;             // ceil(N / 128)
+  int nblocks;         // ntm * ntn
+};
+
+// 16-byte chunk c of a 64-byte staged row sits at c ^ ((row >> 2) & 3): the
+// 16 rows that 16 lanes read at one chunk then cover all 64 banks.
+DEV int pj_phys(int row, int ch) { return ch ^ ((row >> 2) & 3); }
+DEV int pj_off(int row, int ch) { return row * PJ_ROWB + (pj_phys(row, ch) << 4); }
+
+// Block -> (token tile, feature tile). xcd_remap gives each XCD a contiguous
+// range of the order; the order runs over groups of PJ_GROUP token tiles and,
+// within a group, feature-tile-major, so the blocks an XCD runs together
+// share their few x tiles in L2 and each W tile is fetched once per group.
+DEV void pj_tile(int bid, const ProjParams& p, int& tm, int& tn) {
+  const int idx = xcd_remap(bid, p.nblocks);
+  const int per = PJ_GROUP * p.ntn;
+  const int grp = idx / per, r = idx - grp * per;
+  const int gm = min(PJ_GROUP, p.ntm - grp * PJ_GROUP);
+  tn = r / gm;
+  tm = grp * PJ_GROUP + (r - tn * gm);
+}
+
+// Wait until this wave's LDS reads have returned (their registers are
+// written), so that a barrier after it also orders them before later
+// global->LDS loads into the same buffer.
+DEV void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[3 * PJ_STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  pj_tile(blockIdx.x, p, tm, tn);
+  const int tok0 = tm * PJ_TM, feat0 = tn * PJ_TN;
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)lds;
+  const unsigned rowbytes = (unsigned)p.D * 2u;
+
+  // Load lane offsets: load I of a stage fills LDS rows 16*(I mod 8) .. +15
+  // of the W tile (I < 8) or of the x tile; lane L writes the 16-byte slot
+  // L of the 1-KB block, which holds logical chunk pj_phys(row, L % 4).
+  unsigned doff[PJ_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PJ_PER_WAVE; ++i) {
+    const int I = wave * PJ_PER_WAVE + i;
+    const bool is_w = I < PJ_A_NI;
+    const int row = (is_w ? I : I - PJ_A_NI) * PJ_RPB + (lane >> 2);
+    const int grow = is_w ? min(feat0 + row, p.N - 1) : min(tok0 + row, p.M - 1);
+    doff[i] = (unsigned)grow * rowbytes + ((unsigned)pj_phys(row, lane & 3) << 4);
+  }
+  auto issue = [&](int step, int stage) {
+    const char* wb = reinterpret_cast<const char*>(p.w) + (size_t)step * PJ_ROWB;
+    const char* xb = reinterpret_cast<const char*>(p.x) + (size_t)step * PJ_ROWB;
+#pragma unroll
+    for (int i = 0; i < PJ_PER_WAVE; ++i) {
+      const int I = wave * PJ_PER_WAVE + i;
+      dma16_saddr(I < PJ_A_NI ? wb : xb, doff[i],
+                  lds0 + (unsigned)(stage * PJ_STAGE_BYTES + I * 1024));
+    }
+  };
+
+  // Fragment reads: lane l takes row l % 32 of a 32-row group, chunk
+  // 2*ks + l/32 (input features 16*ks + 8*(l/32) .. +7); the swizzle reads
+  // row bits 2..3 only, so the group enters as a plain offset.
+  int roff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) roff[ks] = pj_off(lane & 31, 2 * ks + (lane >> 5));
+  const int wm = wave >> 1, wn = wave & 1;
+  const int a_off = wn * 64 * PJ_ROWB;                // this wave's 64 W rows
+  const int b_off = PJ_A_BYTES + wm * 128 * PJ_ROWB;  // this wave's 128 x rows
+
+  // This wave's 64 output features are one (projection, head) block; its
+  // bias is read before the main loop so that the load's latency is hidden.
+  const int ph = (feat0 >> 6) + wn;
+  const bool ph_ok = ph * 64 < p.N;
+  const int g = lane >> 5;
+  bf16x4 bq[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      bq[f][jq] = bf16x4{};
+      if (p.bias && ph_ok)
+        bq[f][jq] = *reinterpret_cast<const bf16x4*>(p.bias + ph * 64 + f * 32 + 8 * jq + 4 * g);
+    }
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[f][t][r] = 0.f;
+
+  auto read_frags = [&](const char* sb, int ks, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      a[f] = *reinterpret_cast<const bf16x8*>(sb + a_off + f * 32 * PJ_ROWB + roff[ks]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      b[t] = *reinterpret_cast<const bf16x8*>(sb + b_off + t * 32 * PJ_ROWB + roff[ks]);
+  };
+  auto mma = [&](const bf16x8 (&a)[2], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[f][t] = mfma_bf16(a[f], b[t], acc[f][t]);
+  };
+
+  // Ring: stage s % 3 holds input features 32s .. 32s+31. The fragments of
+  // the next 16-feature step are read while the current step's MFMAs run;
+  // the barrier that hands over the next stage sits before the last step,
+  // so the next stage's first fragments are read under its MFMAs too.
+  const int nk = p.D / PJ_TK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 1) wait_vmcnt<PJ_PER_WAVE>();
+  else wait_vmcnt<0>();
+  wg_barrier();  // stage 0 has landed for every wave
+  if (nk > 2) issue(2, 2);
+  bf16x8 a0[2], b0[4], a1[2], b1[4];
+  read_frags(lds, 0, a0, b0);
+  int stage = 0;
+  for (int s = 0; s < nk; ++s) {
+    const char* sb = lds + stage * PJ_STAGE_BYTES;
+    const int nstage = stage == 2 ? 0 : stage + 1;
+    read_frags(sb, 1, a1, b1);
+    mma(a0, b0);
+    if (s + 1 < nk) {
+      if (s + 2 < nk) wait_vmcnt<PJ_PER_WAVE>();
+      else wait_vmcnt<0>();
+      wait_lgkm0();  // this wave's reads of stage s have returned
+      wg_barrier();  // stage s+1 has landed for every wave; stage s is consumed
+      if (s + 3 < nk) issue(s + 3, stage);
+      read_frags(lds + nstage * PJ_STAGE_BYTES, 0, a0, b0);
+    }
+    mma(a1, b1);
+    stage = nstage;
+  }
+
+  // Epilogue. Lane l holds token column l % 32 of each 32-token group and,
+  // in register j, feature 8*(j/4) + 4*(l/32) + j%4 of each 32-feature group.
+  // Each wave stages its 128 x 64 tile (bias added, rounded to bf16) in its
+  // own 16 KB of the ring as [token][64 features], 8-byte unit u of row r at
+  // u ^ ((r >> 1) & 15) (conflict-free for both access patterns), then
+  // writes whole 128-byte token rows: 8 rows per store instruction.
+  wait_lgkm0();
+  wg_barrier();  // every wave is done with the ring
+  if (!ph_ok) return;
+  char* st = lds + wave * (128 * 128);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = t * 32 + (lane & 31);
+    const int k = (row >> 1) & 15;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        bf16x4 o4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o4[u] = (__bf16)(acc[f][t][4 * jq + u] + (float)bq[f][jq][u]);
+        const int unit = (f * 8 + 2 * jq + g) ^ k;
+        *reinterpret_cast<bf16x4*>(st + row * 128 + unit * 8) = o4;
+      }
+  }
+  wait_lgkm0();  // the wave reads back what its other lanes wrote
+  const int proj = ph / p.H, h = ph - proj * p.H;
+  const int T = tok0 + wm * 128;  // this wave's first token
+  __bf16* obase = p.out + ((size_t)proj * p.B * p.H + h) * (size_t)p.n * 64;
+  const size_t item_stride = (size_t)p.H * p.n * 64;
+  const int item0 = T / p.n, pos0 = T - item0 * p.n;
+  const bool one_item = pos0 + 128 <= p.n;  // wave-uniform
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 8 + (lane >> 3), c = lane & 7;
+    const int k = (row >> 1) & 15;
+    uint4 v = *reinterpret_cast<const uint4*>(st + row * 128 + ((c ^ (k >> 1)) << 4));
+    if (k & 1) v = uint4{v.z, v.w, v.x, v.y};
+    const int tok = T + row;
+    if (tok < p.M) {
+      int b = item0, i = pos0 + row;
+      if (!one_item) { b = tok / p.n; i = tok - b * p.n; }
+      *reinterpret_cast<uint4*>(obase + b * item_stride + (size_t)i * 64 + c * 8) = v;
+    }
+  }
+}
+
+}  // namespace swattn

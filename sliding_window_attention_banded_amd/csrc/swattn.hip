@@ -15,6 +15,7 @@
 #include "swattn.h"
 #include "kernels.hpp"
 #include "backward.hpp"
+#include "project.hpp"
 
 using namespace swattn;
 
@@ -454,5 +455,39 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch bwd_gred");
   }
+  return SWATTN_OK;
+}
+
+extern "C" int swattn_project(const void* x, const void* w, const void* bias, void* out,
+                              int batch, int n, int d_model, int heads, int nproj, int dtype,
+                              void* stream) {
+  g_last_error.clear();
+  if (!x || !w || !out) return fail(SWATTN_ERR_INVALID_ARG, "x, w and out must not be NULL");
+  if (batch < 1 || n < 1 || heads < 1 || nproj < 1 || d_model < 1)
+    return fail(SWATTN_ERR_INVALID_ARG, "batch, n, heads, nproj and d_model must be >= 1");
+  if (dtype != SWATTN_BF16) return fail(SWATTN_ERR_UNSUPPORTED, "the projection is bf16 only");
+  if (d_model % PJ_TK) return fail(SWATTN_ERR_UNSUPPORTED, "d_model must be a multiple of 32");
+  const long M = (long)batch * n, N = (long)nproj * heads * HD;
+  // 32-bit byte offsets into x and w
+  if (M * d_model * 2 >= (1L << 31) || N * d_model * 2 >= (1L << 31))
+    return fail(SWATTN_ERR_UNSUPPORTED, "x and w must each be smaller than 2 GiB");
+  for (const void* ptr : {x, w, bias, (const void*)out})
+    if (ptr && !aligned16(ptr)) return fail(SWATTN_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const size_t xb = (size_t)M * d_model * 2, wb = (size_t)N * d_model * 2, ob = (size_t)M * N * 2;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, bias, (size_t)N * 2))
+    return fail(SWATTN_ERR_INVALID_ARG, "out overlaps an input");
+  const long ntm = (M + PJ_TM - 1) / PJ_TM, ntn = (N + PJ_TN - 1) / PJ_TN;
+  if (ntm * ntn > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+  ProjParams pp;
+  pp.x = static_cast<const __bf16*>(x);
+  pp.w = static_cast<const __bf16*>(w);
+  pp.bias = static_cast<const __bf16*>(bias);
+  pp.out = static_cast<__bf16*>(out);
+  pp.M = (int)M; pp.N = (int)N; pp.D = d_model; pp.n = n; pp.B = batch; pp.H = heads;
+  pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn);
+  hipLaunchKernelGGL(proj_gemm, dim3((unsigned)pp.nblocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), pp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch proj_gemm");
   return SWATTN_OK;
 }

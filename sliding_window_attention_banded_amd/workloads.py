@@ -19,7 +19,7 @@ from dataclasses import dataclass, field, replace
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "DTYPES", "item_globals", "has_globals",
-           "global_union"]
+           "global_union", "make_projection_inputs"]
 
 DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
@@ -164,3 +164,19 @@ def make_inputs(wl: Workload, seed: int, kind: str = "normal"):
     for r in ("qg", "kg", "vg"):
         out.setdefault(r, None)
     return out
+
+
+def make_projection_inputs(batch, n, d_model, heads, nproj, seed, bias=True):
+    """Seeded CPU bf16 tensors for the projections in front of the attention:
+    x [batch, n, d_model] ~ N(0, 1) (a normalised layer input), weight
+    [nproj*heads*64, d_model] ~ N(0, 1/d_model) (the usual fan-in scaling,
+    so that the projections come out of order one) and bias
+    [nproj*heads*64] ~ N(0, 0.1^2) or None. Draw order: x, weight, bias;
+    drawn in float32, rounded to nearest-even bf16."""
+    gen = torch.Generator(device="cpu").manual_seed(20_000 + int(seed))
+    N = nproj * heads * 64
+    x = torch.randn((batch, n, d_model), generator=gen, dtype=torch.float32)
+    w = torch.randn((N, d_model), generator=gen, dtype=torch.float32) / d_model ** 0.5
+    b = torch.randn((N,), generator=gen, dtype=torch.float32) * 0.1 if bias else None
+    bf = lambda t: None if t is None else t.to(torch.bfloat16).contiguous()
+    return bf(x), bf(w), bf(b)

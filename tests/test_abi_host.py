@@ -76,3 +76,28 @@ def test_null_arguments(lib):
     assert lib.swattn_create(ctypes.byref(p), None) == 1
     assert lib.swattn_forward(None, *([None] * 9)) == 1
     assert lib.swattn_destroy(None) == 0
+
+
+# swattn_project: every case below fails validation before any launch (the
+# pointers are never dereferenced).
+_X, _W, _O = 0x100000, 0x800000, 0x4000000
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(out=None), 1),
+    (dict(batch=0), 1), (dict(n=0), 1), (dict(heads=0), 1), (dict(nproj=0), 1),
+    (dict(d_model=0), 1),
+    (dict(dtype=1), 2), (dict(d_model=80), 2),
+    (dict(batch=1 << 20, n=1 << 10), 2),   # x of 2^30 * 64 * 2 bytes
+    (dict(x=_X + 8), 4), (dict(bias=_W + 0x10000 + 8), 4), (dict(out=_O + 2), 4),
+    (dict(out=_X + 64), 1),                # out overlaps x
+])
+def test_project_rejects_bad_parameters(lib, args, code):
+    a = dict(x=_X, w=_W, bias=None, out=_O, batch=2, n=16, d_model=64, heads=2,
+             nproj=3, dtype=0)
+    a.update(args)
+    lib.swattn_project.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    st = lib.swattn_project(a["x"], a["w"], a["bias"], a["out"], a["batch"], a["n"],
+                            a["d_model"], a["heads"], a["nproj"], a["dtype"], None)
+    assert st == code
+    assert lib.swattn_last_error().decode() != ""
