@@ -152,17 +152,19 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
     for (int t = 0; t < 4; ++t)
       b[t] = *reinterpret_cast<const bf16x8*>(sb + b_off + t * 32 * PJ_ROWB + roff[ks]);
   };
-  auto mma = [&](const bf16x8 (&a)[2], const bf16x8 (&b)[4]) {
+  // MFMAs k0 .. k1-1 of one 16-feature step, k = 4 * (feature group) + token group
+  auto mma = [&](const bf16x8 (&a)[2], const bf16x8 (&b)[4], int k0, int k1) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[f][t] = mfma_bf16(a[f], b[t], acc[f][t]);
+    for (int k = 0; k < 8; ++k)
+      if (k >= k0 && k < k1) acc[k / 4][k % 4] = mfma_bf16(a[k / 4], b[k % 4], acc[k / 4][k % 4]);
   };
 
-  // Ring: stage s % 3 holds input features 32s .. 32s+31. The fragments of
-  // the next 16-feature step are read while the current step's MFMAs run;
-  // the barrier that hands over the next stage sits before the last step,
-  // so the next stage's first fragments are read under its MFMAs too.
+  // Ring: stage s % 3 holds input features 32s .. 32s+31. Per stage: the
+  // second 16-feature step's fragments are read under the first step's
+  // MFMAs; the barrier that hands over the next stage and the loads that
+  // refill this one go between the halves of the second step's MFMAs, and
+  // the next stage's first fragments are read under its second half. The
+  // last stage is peeled off so that the loop body has one path.
   const int nk = p.D / PJ_TK;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
@@ -173,22 +175,24 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
   bf16x8 a0[2], b0[4], a1[2], b1[4];
   read_frags(lds, 0, a0, b0);
   int stage = 0;
-  for (int s = 0; s < nk; ++s) {
+  for (int s = 0; s + 1 < nk; ++s) {
     const char* sb = lds + stage * PJ_STAGE_BYTES;
     const int nstage = stage == 2 ? 0 : stage + 1;
     read_frags(sb, 1, a1, b1);
-    mma(a0, b0);
-    if (s + 1 < nk) {
-      if (s + 2 < nk) wait_vmcnt<PJ_PER_WAVE>();
-      else wait_vmcnt<0>();
-      wait_lgkm0();  // this wave's reads of stage s have returned
-      wg_barrier();  // stage s+1 has landed for every wave; stage s is consumed
-      if (s + 3 < nk) issue(s + 3, stage);
-      read_frags(lds + nstage * PJ_STAGE_BYTES, 0, a0, b0);
-    }
-    mma(a1, b1);
+    mma(a0, b0, 0, 8);
+    if (s + 2 < nk) wait_vmcnt<PJ_PER_WAVE>();
+    else wait_vmcnt<0>();
+    wait_lgkm0();  // this wave's reads of stage s have returned
+    wg_barrier();  // stage s+1 has landed for every wave; stage s is consumed
+    mma(a1, b1, 0, 4);
+    if (s + 3 < nk) issue(s + 3, stage);
+    read_frags(lds + nstage * PJ_STAGE_BYTES, 0, a0, b0);
+    mma(a1, b1, 4, 8);
     stage = nstage;
   }
+  read_frags(lds + stage * PJ_STAGE_BYTES, 1, a1, b1);
+  mma(a0, b0, 0, 8);
+  mma(a1, b1, 0, 8);
 
   // Epilogue. Lane l holds token column l % 32 of each 32-token group and,
   // in register j, feature 8*(j/4) + 4*(l/32) + j%4 of each 32-feature group.
@@ -222,6 +226,23 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
   const size_t item_stride = (size_t)p.H * p.n * 64;
   const int item0 = T / p.n, pos0 = T - item0 * p.n;
   const bool one_item = pos0 + 128 <= p.n;  // wave-uniform
+  if (one_item && T + 128 <= p.M) {
+    // every row exists and the 128 rows are consecutive in out: read the
+    // whole tile back first, then store it without per-lane conditions
+    __bf16* orow = obase + item0 * item_stride + (size_t)pos0 * 64;
+    uint4 v[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 8 + (lane >> 3), c = lane & 7;
+      const int k = (row >> 1) & 15;
+      v[it] = *reinterpret_cast<const uint4*>(st + row * 128 + ((c ^ (k >> 1)) << 4));
+      if (k & 1) v[it] = uint4{v[it].z, v[it].w, v[it].x, v[it].y};
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it)
+      *reinterpret_cast<uint4*>(orow + (size_t)(it * 8 + (lane >> 3)) * 64 + (lane & 7) * 8) = v[it];
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int row = it * 8 + (lane >> 3), c = lane & 7;
