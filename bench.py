@@ -6,7 +6,11 @@ pass, merge) over one batch of the workload, inputs already resident in HBM.
 Prints ONE JSON line. The throughput `value` is band TFLOP/s (4*d*sum of
 window keys per row, the closed form of the Longformer window), measured over
 K steps that rotate through enough input sets to exceed the 256 MB Infinity
-Cache; the warm (single input set) figure is reported beside it.
+Cache; the warm (single input set) figure is reported beside it. The same
+line carries the backward pass of the workload ("backward") and the
+projections in front of it ("projection": Q, K, V and, with global tokens,
+Qg, Kg, Vg from an input of d_model = heads*64 features), each timed the
+same way.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
