@@ -9,7 +9,8 @@ Longformer-base encoder shape, the autoregressive character-LM shapes of
 section 4 (windows per layer, dilation on two heads, staged sequence length up
 to 23,040), the QA shape of section 3-1 "Global Attention" (question tokens as
 globals) and the LED encoder of section 7 (16K tokens, window 1024, one global
-token). No dataset is read; every tensor is drawn from a seeded generator.
+token) with its decoder's left-only self-attention. No dataset is read; every
+tensor is drawn from a seeded generator.
 """
 
 from __future__ import annotations
@@ -108,6 +109,11 @@ WORKLOADS = {
     "led_b1_h12_n16384_w1024_g1": Workload(
         "led_b1_h12_n16384_w1024_g1", 1, 12, 16384, 64, _per_head(12, 1024),
         _per_head(12, 1), False, (0,)),
+    # LED decoder self-attention: left-only over 1024 output tokens, every
+    # earlier token visible (a causal window of 2n covers the whole prefix)
+    "led_decoder_b1_h12_n1024_causal": Workload(
+        "led_decoder_b1_h12_n1024_causal", 1, 12, 1024, 64, _per_head(12, 2048),
+        _per_head(12, 1), True, ()),
 }
 
 

@@ -132,6 +132,7 @@ def test_backward_small(wl, kind):
     ("arlm_b1_h12_n8192_w512_causal_dil2", [(0, 3), (0, 11)]),
     ("qa_b4_h12_n4096_w512_g64", [(3, 7)]),
     ("qa_b4_h12_n4096_w512_gper", [(2, 1), (3, 5)]),
+    ("led_decoder_b1_h12_n1024_causal", [(0, 0), (0, 11)]),
 ])
 @pytest.mark.parametrize("kind", ["normal", "sharp"])
 def test_backward_full_size_slices(name, bh, kind):

@@ -95,7 +95,8 @@ def _sample_rows(wl, count=48, seed=0):
 
 FULL = ["encoder_b2_h12_n4096_w512_g1", "encoder_b2_h12_n4096_w512",
         "arlm_b1_h12_n8192_w512_causal_dil2", "arlm_b1_h8_n23040_w1024_causal_dil4",
-        "qa_b4_h12_n4096_w512_g64", "qa_b4_h12_n4096_w512_gper", "led_b1_h12_n16384_w1024_g1"]
+        "qa_b4_h12_n4096_w512_g64", "qa_b4_h12_n4096_w512_gper", "led_b1_h12_n16384_w1024_g1",
+        "led_decoder_b1_h12_n1024_causal"]
 
 
 @pytest.mark.parametrize("name", FULL)
