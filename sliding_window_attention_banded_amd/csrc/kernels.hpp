@@ -242,18 +242,7 @@ DEV void load_q(QFrag<float>& qf, const float* row, int g) {
   for (int s = 0; s < 32; ++s) qf.v[s] = row[2 * s + g];
 }
 
-// S^T for one 32-key unit (rows 32*kh .. 32*kh+31 of the LDS tile).
-DEV f32x16 score_unit(const char* kbuf, int kh, const QFrag<__bf16>& qf, int lane) {
-  const int g = lane >> 5;
-  const int row = kperm16(lane & 31) + 32 * kh;
-  f32x16 s = {};
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    bf16x8 a = *reinterpret_cast<const bf16x8*>(kbuf + ElemTraits<__bf16>::lds_off(row, 2 * st + g));
-    s = mfma_bf16(a, qf.v[st], s);
-  }
-  return s;
-}
+// fp32 path: S^T for one 32-key unit (rows 32*kh .. 32*kh+31 of the LDS tile).
 DEV f32x16 score_unit(const char* kbuf, int kh, const QFrag<float>& qf, int lane) {
   const int g = lane >> 5;
   const int row = kperm32(lane & 31) + 32 * kh;
@@ -264,33 +253,8 @@ DEV f32x16 score_unit(const char* kbuf, int kh, const QFrag<float>& qf, int lane
   return s;
 }
 
-// O^T += V^T P^T for one 32-key unit; b[sp] holds the bf16 probabilities of
-// keys 16*sp + 8g .. +7 (the B operand, straight from the accumulator layout
-// of score_unit).
-DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const bf16x8 (&b)[2], int lane) {
-  const int g = lane >> 5;
-  const int i16 = lane & 15;
-#pragma unroll
-  for (int sp = 0; sp < 2; ++sp) {
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh) {
-      // Source lane i16 of each 16-lane group points at 4 d-contiguous
-      // elements of key key0 + i16/4, columns d0 + 4*(i16%4) ..+3; the
-      // transposed read hands lane i16 the 4 keys at column d0 + i16.
-      const int d0 = 32 * dh + 16 * ((lane >> 4) & 1);
-      const int col = d0 + 4 * (i16 & 3);
-      const int key0 = 32 * kh + 16 * sp + 8 * g;
-      const int row0 = key0 + (i16 >> 2), row1 = row0 + 4;
-      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(vbuf + ElemTraits<__bf16>::lds_off(row0, col >> 3) + ((col & 7) << 1)));
-      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(vbuf + ElemTraits<__bf16>::lds_off(row1, col >> 3) + ((col & 7) << 1)));
-      const s16x8 a = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc.o[dh] = mfma_bf16(__builtin_bit_cast(bf16x8, a), b[sp], acc.o[dh]);
-    }
-  }
-}
-DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane, float) {
+// fp32 path: O^T += V^T P^T for one 32-key unit.
+DEV void pv_unit(WaveAcc& acc, const char* vbuf, int kh, const f32x16& p, int lane) {
   const int g = lane >> 5;
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
@@ -328,7 +292,7 @@ template <class T> DEV constexpr int key_of_reg(int j, int g) {
 // most the 2^-8 relative rounding of a weight.
 constexpr float RESCALE_LOG2 = 8.0f;
 
-template <class T>
+// fp32 path: online softmax of one 32-key unit and O += P V.
 DEV void softmax_pv_unit(WaveAcc& acc, f32x16 s, const char* vbuf, int kh, int lane, float c2) {
   float mx = s[0];
 #pragma unroll
@@ -346,39 +310,21 @@ DEV void softmax_pv_unit(WaveAcc& acc, f32x16 s, const char* vbuf, int kh, int l
     // a row with every key masked so far has m = -inf and only -inf scores
     acc.moff = acc.m == -__builtin_inff() ? 0.f : -acc.m * c2;
   }
-  if constexpr (sizeof(T) == 2) {
-    // P in bf16 (round to nearest even) is the MFMA operand; the row sum adds
-    // up exactly these rounded weights, two at a time.
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x8 b[2];
-    float l = acc.l;
+  float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
-      const bf16x2 t = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-      l = __builtin_amdgcn_fdot2_f32_bf16(t, one, l, false);
-      b[j >> 3][j & 7] = t[0];
-      b[j >> 3][(j & 7) + 1] = t[1];
-    }
-    acc.l = l;
-    pv_unit(acc, vbuf, kh, b, lane);
-  } else {
-    float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
-      s[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
-      l0 += s[j];
-      l1 += s[j + 1];
-    }
-    acc.l += l0 + l1;
-    pv_unit(acc, vbuf, kh, s, lane, T{});
+  for (int j = 0; j < 16; j += 2) {
+    s[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
+    s[j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
+    l0 += s[j];
+    l1 += s[j + 1];
   }
+  acc.l += l0 + l1;
+  pv_unit(acc, vbuf, kh, s, lane);
 }
 
-// Pieces of a 32-key unit for the software-pipelined ring: fragments are
-// loaded from LDS well before they are used.
+// bf16 path: the pieces of a 32-key unit as the ring uses them. The K and V
+// fragments are read from LDS into registers ahead of the MFMAs (the V reads
+// are in flight during the softmax).
 struct KFrag { bf16x8 v[4]; };      // A operand of S^T, 4 k-steps of 16 d
 struct VFrag { bf16x8 a[2][2]; };   // A operand of O^T, [16-key step][d half]
 struct PFrag { bf16x8 b[2]; };      // B operand of O^T, [16-key step]
@@ -621,20 +567,6 @@ DEV void tile_commit(const TileRegs<T, NT>& tr, char* klds, char* vlds, int tid)
   }
 }
 
-// Fetch 64 rows kk = kb0 .. kb0+63 (clamped to kend-1) of K and V.
-template <class T, int NT>
-DEV void plain_fetch(TileRegs<T, NT>& tr, const char* kb, const char* vb, int kb0, int kend, int tid) {
-  constexpr int CPR = ElemTraits<T>::CPR;
-#pragma unroll
-  for (int u = 0; u < TileRegs<T, NT>::NC; ++u) {
-    const int c = tid + NT * u;
-    const int kk = min(kb0 + c / CPR, kend - 1);
-    const long off = (long)kk * ElemTraits<T>::ROWB + (c % CPR) * 16;
-    tr.k[u] = *reinterpret_cast<const uint4*>(kb + off);
-    tr.v[u] = *reinterpret_cast<const uint4*>(vb + off);
-  }
-}
-
 // ----------------------------------------------------------------------------
 // The key-tile ring shared by band blocks and global-row blocks.
 
@@ -712,7 +644,7 @@ DEV void ring_step(int tb, WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, c
     } else {
       f32x16 sc = score_unit(cur, kh, qf, c.lane);
       if (!pol.interior(ku)) pol.template mask<T>(sc, ku, c.g);
-      softmax_pv_unit<T>(acc, sc, cur + TILEB, kh, c.lane, c.c2);
+      softmax_pv_unit(acc, sc, cur + TILEB, kh, c.lane, c.c2);
     }
   }
 }
@@ -838,7 +770,7 @@ DEV void glob_cols_tile(WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, cons
       if (!(kp <= lim) || inband) s[j] = -__builtin_inff();
     }
     if constexpr (sizeof(T) == 2) pv_from(acc, load_vfrag(stage + TILEB, kh, c.ll), softmax_p(acc, s, c.c2));
-    else softmax_pv_unit<T>(acc, s, stage + TILEB, kh, c.lane, c.c2);
+    else softmax_pv_unit(acc, s, stage + TILEB, kh, c.lane, c.c2);
   }
 }
 
