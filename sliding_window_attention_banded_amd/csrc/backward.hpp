@@ -75,7 +75,7 @@ struct BwdParams {
   int n, H;
   int causal;
   int nsplit, ksplit, nqb, ngroup;  // dQg blocks (as in the forward's global rows)
-  int nchunk;                       // query chunks of the global-column blocks
+  int nchunk, gcol_qc;              // query chunks of the global-column blocks, their size
   int nkgb;                         // groups of 4 x 32 global keys
   // block counts of bwd_main: band query blocks (nq), band key blocks (nq),
   // dQg blocks, dKg/dVg blocks, global-column blocks
@@ -84,7 +84,15 @@ struct BwdParams {
   float scale;
 };
 
-constexpr int GCOL_QC = 512;  // query positions per global-column block
+// Query positions per global-column block, and keys per dQg block. With at
+// most 32 global tokens per item those blocks compute little and mostly wait
+// on memory, so they are made fewer and longer (about a quarter of the
+// sequence per global-column block, within [512, 4096], and at least 1024
+// keys per dQg block), holding fewer workgroup slots; longer still and they
+// become the critical path. Larger sets keep the finer split.
+constexpr int GCOL_QC = 512;
+constexpr int GCOL_QC_MAX = 4096;
+constexpr int GQ_KEYS_SMALL_G = 1024;
 
 // ----------------------------------------------------------------------------
 // Row statistics: 8 lanes per row, 8 elements each.
@@ -657,7 +665,7 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
 
 // ----------------------------------------------------------------------------
 // Global columns: the dK[G], dV[G] terms of the non-global rows whose band
-// does not already hold the key (key blocks over query chunks of GCOL_QC
+// does not already hold the key (key blocks over query chunks of gcol_qc
 // positions; wave w holds global keys 32 (4 kg + w) ..).
 
 struct GcolPol {
@@ -704,8 +712,8 @@ DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char*
   const int gi = kgi * 32 + (lane & 31);
   const int gpos = gs.idx[min(gi, gs.n - 1)];
   const int gmin = gs.idx[min(kgi * 32, gs.n - 1)];
-  const int qbeg = ch * GCOL_QC;
-  const int qend = min(p.n, qbeg + GCOL_QC);
+  const int qbeg = ch * p.gcol_qc;
+  const int qend = min(p.n, qbeg + p.gcol_qc);
   const int nband = (qend - qbeg + KT - 1) / KT;
   const long roff = base + (long)gpos * ROWB;
 

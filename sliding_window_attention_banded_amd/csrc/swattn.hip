@@ -59,7 +59,8 @@ struct swattn_plan {
   float* bwd_lse2;        // [B*H][n] backward row statistics (bf16 plans)
   float* bwd_dd;          // [B*H][n]
   // backward, global tokens (bf16 plans with n_global > 0)
-  int ngp, ng32, nchunk, nkgb, n_gkv, n_gcol;
+  int ngp, ng32, nchunk, gcol_qc, nkgb, n_gkv, n_gcol;
+  int bwd_nsplit, bwd_ksplit, n_gq;  // dQg blocks: key chunks (no more than the forward's)
   float* bwd_glse2;       // [B*H][ngp], +inf padding
   float* bwd_gdd;         // [B*H][ngp], 0 padding
   float* bwd_part_gkv;    // [B*H][nchunk][ng32][128]
@@ -200,12 +201,21 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const bool bwd_g = bwd && pl->ng > 0;
   pl->ngp = bwd_g ? (pl->ng + KT - 1) / KT * KT : 0;
   pl->ng32 = bwd_g ? (pl->ng + 31) / 32 * 32 : 0;
-  pl->nchunk = bwd_g ? (p->n + GCOL_QC - 1) / GCOL_QC : 0;
+  const bool small_g = pl->ng <= 32;
+  pl->gcol_qc = GCOL_QC;
+  if (small_g) pl->gcol_qc = std::min(GCOL_QC_MAX, std::max(GCOL_QC, (p->n / 4 + GCOL_QC - 1) / GCOL_QC * GCOL_QC));
+  pl->nchunk = bwd_g ? (p->n + pl->gcol_qc - 1) / pl->gcol_qc : 0;
+  // the dQg partials live in the forward's global-row workspace: at most as
+  // many key chunks as the forward has
+  pl->bwd_ksplit = pl->ksplit;
+  if (bwd_g && small_g) pl->bwd_ksplit = std::max(pl->ksplit, GQ_KEYS_SMALL_G);
+  pl->bwd_nsplit = bwd_g ? (p->n + pl->bwd_ksplit - 1) / pl->bwd_ksplit : 0;
+  pl->n_gq = bwd_g ? (int)((long)pl->bwd_nsplit * pl->ngroup * bh) : 0;
   pl->nkgb = bwd_g ? ((pl->ng + 31) / 32 + BAND_WAVES - 1) / BAND_WAVES : 0;
   {
     const long n_gkv = bwd_g ? bh * ((p->n + BM * GKV_GROUPS - 1) / (BM * GKV_GROUPS)) : 0;
     const long n_gcol = bwd_g ? bh * (long)pl->nchunk * pl->nkgb : 0;
-    const long nbwd = 2 * nband_blocks + (bwd_g ? (long)pl->nglob_blocks : 0) + n_gkv + n_gcol;
+    const long nbwd = 2 * nband_blocks + (long)pl->n_gq + n_gkv + n_gcol;
     if (nbwd > 0x7fffffffL) {
       delete pl;
       return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
@@ -437,10 +447,10 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   bp.uni_nqb = pl->uni_nqb;
   bp.gidx = pl->gidx; bp.goff = pl->goff; bp.ng = pl->ng; bp.ngp = pl->ngp; bp.ng32 = pl->ng32;
   bp.n = pl->n; bp.H = pl->H; bp.causal = pl->causal;
-  bp.nsplit = pl->nsplit; bp.ksplit = pl->ksplit; bp.nqb = pl->nqb; bp.ngroup = pl->ngroup;
-  bp.nchunk = pl->nchunk; bp.nkgb = pl->nkgb;
+  bp.nsplit = pl->bwd_nsplit; bp.ksplit = pl->bwd_ksplit; bp.nqb = pl->nqb; bp.ngroup = pl->ngroup;
+  bp.nchunk = pl->nchunk; bp.gcol_qc = pl->gcol_qc; bp.nkgb = pl->nkgb;
   bp.nq = pl->nband_blocks;
-  bp.n_gq = pl->ng > 0 ? pl->nglob_blocks : 0;
+  bp.n_gq = pl->n_gq;
   bp.n_gkv = pl->n_gkv; bp.n_gcol = pl->n_gcol;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   const long rows = (long)pl->B * pl->H * pl->n;
