@@ -68,6 +68,12 @@ typedef struct swattn_params {
                                     at 0, never decrease and end at n_global <= batch*n):
                                     the QA setting of section 3-1, where each example's
                                     question tokens are its global tokens. */
+  int32_t key_split;           /* 0: the library decides; 1: never; 2..16: the band keys of
+                                  every 128-row tile are shared out over this many
+                                  workgroups, whose partial results a merge kernel
+                                  combines (for problems too small to fill the GPU; the
+                                  result is the same up to fp32 rounding). Zero-initialising
+                                  the struct selects 0. */
 } swattn_params;
 
 typedef struct swattn_plan swattn_plan;

@@ -37,7 +37,8 @@ class _Params(ctypes.Structure):
                 ("causal", ctypes.c_int32),
                 ("global_idx", ctypes.POINTER(ctypes.c_int32)),
                 ("n_global", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("global_offsets", ctypes.POINTER(ctypes.c_int32))]
+                ("global_offsets", ctypes.POINTER(ctypes.c_int32)),
+                ("key_split", ctypes.c_int32)]
 
 
 def library_path():
@@ -97,11 +98,13 @@ class Plan:
     ``window`` and ``dilation`` are per head (a scalar is broadcast);
     ``global_idx`` lists the global-token positions shared by all batch items
     and heads, or gives one such list per batch item. Tensors are
-    [B, H, n, 64] contiguous CUDA tensors in ``dtype``.
+    [B, H, n, 64] contiguous CUDA tensors in ``dtype``. ``key_split``: 0 lets
+    the library share the band keys over several workgroups when the problem
+    is too small to fill the GPU; 1 never does; k >= 2 always uses k parts.
     """
 
     def __init__(self, batch, heads, n, d=64, window=512, dilation=1,
-                 causal=False, global_idx=(), dtype=torch.bfloat16):
+                 causal=False, global_idx=(), dtype=torch.bfloat16, key_split=0):
         self._lib = load_library()
         if dtype not in _DT:
             raise SwattnError(ERR_UNSUPPORTED, f"dtype {dtype} not supported")
@@ -135,7 +138,8 @@ class Plan:
         p = _Params(batch, heads, n, d, W, D, int(bool(causal)),
                     ctypes.cast(G, ctypes.POINTER(ctypes.c_int32)) if G else None,
                     len(gl), _DT[dtype],
-                    ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O else None)
+                    ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O else None,
+                    int(key_split))
         h = ctypes.c_void_p()
         _check(self._lib, self._lib.swattn_create(ctypes.byref(p), ctypes.byref(h)),
                "swattn_create")

@@ -85,12 +85,20 @@ struct BandParams {
   const int* gidx;       // sorted G: one set, or the batch items' sets one after another
   const int* goff;       // [B+1] offsets of the per-item sets in gidx, or NULL (one set)
   int ng;                // |G| (one set), or the largest per-item |G|
+  // key split: each band tile's key tiles are shared out over `parts`
+  // workgroups that write unnormalised partials (o[64], m, l) to
+  // part[(b*h*n + position) * parts + k][68] for band_merge (parts = 1: none)
+  int parts;
+  float* part;
   int H;
   int n;
   int causal;
   float c2;     // scale * log2(e)
   float scale;  // 1/sqrt(64)
 };
+
+constexpr int PART_STRIDE = 68;  // floats per partial record: o[64], m, l, 2 pad
+constexpr int MAX_KEY_SPLIT = 16;
 
 struct GlobalParams {
   const void* qg;
@@ -775,7 +783,8 @@ DEV void glob_cols_tile(WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, cons
 }
 
 template <class T>
-DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* st2, int (*gmeta)[KT]) {
+DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st1, char* st2,
+                    int (*gmeta)[KT]) {
   constexpr int ROWB = ElemTraits<T>::ROWB;
   constexpr int CPR = ElemTraits<T>::CPR;
   constexpr int TILEB = KT * ROWB;
@@ -790,7 +799,7 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
   const TileRec td = decode_tile(p, tile);
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, td.bh / p.H);
   const int* gix = gs.idx;
-  const int ngb = gs.n;
+  const int ngb = part == 0 ? gs.n : 0;  // the global columns go with the first key part
   int gq[4] = {0, 0, 0, 0};
   int gm = 0;
   if (BF16 && ngb > 0) {
@@ -807,6 +816,8 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
   const int kbeg = max(0, q0 - half);
   const int kend = min(nr, q0 + BM + right);
   const int nband = (kend - kbeg + KT - 1) / KT;  // >= 1: row q0 sees itself
+  // with a key split this workgroup takes band tiles t0 .. t1-1 (maybe none)
+  const int t0 = part * nband / p.parts, t1 = (part + 1) * nband / p.parts;
 
   // this wave's query rows and key range (residue-local)
   const int qw0 = q0 + 32 * wave;
@@ -819,7 +830,7 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
   const int lim = p.causal ? pos_q : 0x7fffffff - 1;
 
   RingCtx c{(unsigned)(uintptr_t)(lds_void*)st0, (unsigned)(uintptr_t)(lds_void*)st1,
-            (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
+            (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg + t0 * KT, kend, t1 - t0, r, dil,
             wave, lane, g, wave_live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
   const BandPol pol{qi, qw0, half, right, nr, wk_lo, wk_hi};
@@ -834,7 +845,7 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
     // 1, and Q. (The gather goes first: the compiler waits for the indices
     // it needs with a count that only knows its own loads.)
     if (ngb > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
-    ring_start<T>(c);
+    if (c.nband > 0) ring_start<T>(c);
     load_q(qf, qrow, g);
     if (ngb > 0) {
       if (tid < KT) gmeta_write(gmeta, gm, tid < ngb, r, dil, tid);
@@ -880,7 +891,7 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
         __syncthreads();
       }
     }
-    ring_start<T>(c);
+    if (c.nband > 0) ring_start<T>(c);
   }
 
   // band tiles through the ring: the loads of the next tiles are in flight
@@ -890,7 +901,12 @@ DEV void band_block(const BandParams& p, int tile, char* st0, char* st1, char* s
 
   if (wave_live) {
     const float ltot = pair_sum(acc.l);
-    if (row_ok) {
+    if (row_ok && p.parts > 1) {
+      // unnormalised partial for band_merge (m = -inf, l = 0 without keys)
+      float* rec = p.part + (((long)bh * p.n + pos_q) * p.parts + part) * PART_STRIDE;
+      store_o(rec, acc, 1.0f, g);
+      if (g == 0) *reinterpret_cast<f32x2*>(rec + HD) = f32x2{acc.m, ltot};
+    } else if (row_ok) {
       const float inv = 1.0f / ltot;
       T* orow = reinterpret_cast<T*>(reinterpret_cast<char*>(p.o) + base + (long)pos_q * ROWB);
       store_o(orow, acc, inv, g);
@@ -984,8 +1000,61 @@ __global__ __launch_bounds__(256, 3) void attn_fwd(BandParams bp, GlobalParams g
   __shared__ __attribute__((aligned(1024))) char st2[NS == 3 ? STAGEB : 1024];
   __shared__ int gmeta[2][KT];  // global-column tile: key position, residue-local index
   const int b = blockIdx.x;
-  if (b < nband_blocks) band_block<T>(bp, xcd_remap(b, nband_blocks), st0, st1, st2, gmeta);
+  if (b < nband_blocks) {
+    // the key parts of one tile are adjacent, so they share an XCD's L2
+    const int lb = xcd_remap(b, nband_blocks);
+    band_block<T>(bp, lb / bp.parts, lb % bp.parts, st0, st1, st2, gmeta);
+  }
   else global_block<T>(gp, b - nband_blocks, st0, st1, st2);
+}
+
+// Merge of the key parts of every row (with a key split): 16 rows per
+// 256-thread block, 16 threads per row, each owning 4 output columns. All
+// parts of a row are loaded at once, then folded by their maxima as in the
+// online softmax; every row has at least its own key, so the total weight is
+// positive.
+DEV void store4(__bf16* dst, f32x4 v) {
+  bf16x4 t;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] = (__bf16)v[e];
+  *reinterpret_cast<bf16x4*>(dst) = t;
+}
+DEV void store4(float* dst, f32x4 v) { *reinterpret_cast<f32x4*>(dst) = v; }
+
+template <class T>
+__global__ __launch_bounds__(256) void band_merge(BandParams p, long rows) {
+  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c4 = (threadIdx.x & 15) * 4;
+  if (row >= rows) return;
+  const float* rec = p.part + row * p.parts * PART_STRIDE;
+  f32x2 ml[MAX_KEY_SPLIT];
+  f32x4 o[MAX_KEY_SPLIT];
+#pragma unroll
+  for (int k = 0; k < MAX_KEY_SPLIT; ++k)
+    if (k < p.parts) {
+      ml[k] = *reinterpret_cast<const f32x2*>(rec + k * PART_STRIDE + HD);
+      o[k] = *reinterpret_cast<const f32x4*>(rec + k * PART_STRIDE + c4);
+    }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < MAX_KEY_SPLIT; ++k)
+    if (k < p.parts) M = fmaxf(M, ml[k][0]);
+  float L = 0.f;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < MAX_KEY_SPLIT; ++k)
+    if (k < p.parts) {
+      // a part with no key of this row has m = -inf, l = 0, o = 0
+      const float f = ml[k][0] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((ml[k][0] - M) * p.c2);
+      L += ml[k][1] * f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A[e] += o[k][e] * f;
+    }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) A[e] *= inv;
+  store4(reinterpret_cast<T*>(p.o) + row * HD + c4, A);
+  if (p.lse && c4 == 0) p.lse[row] = M * p.scale + __logf(L);
 }
 
 constexpr int MAX_SPLIT = 256;

@@ -49,6 +49,8 @@ struct swattn_plan {
   int nband_blocks;       // band workgroups (explicit tiles, or the uniform decode)
   int uni_half, uni_right, uni_dil, uni_nqb;  // every head alike: no tile list
   int nsplit, ksplit, nqb, ngroup, nglob_blocks;
+  int parts;              // key split of the band tiles (1: none)
+  float* band_part;       // [B*H*n][parts][68] partials, NULL without a split
   void* dev_mem;          // one allocation, carved below
   TileRec* tiles;         // [nband_blocks], NULL with the uniform decode
   int* gidx;              // [n_global]: one sorted set, or the items' sorted sets
@@ -90,6 +92,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   if (p->batch < 1 || p->heads < 1) return fail(SWATTN_ERR_INVALID_ARG, "batch and heads must be >= 1");
   if (p->n < 1 || p->n > (1 << 24)) return fail(SWATTN_ERR_INVALID_ARG, "n must be in [1, 2^24]");
   if (p->causal != 0 && p->causal != 1) return fail(SWATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->key_split < 0 || p->key_split > MAX_KEY_SPLIT)
+    return fail(SWATTN_ERR_INVALID_ARG, "key_split must be in [0, 16]");
   if (!p->window || !p->dilation) return fail(SWATTN_ERR_INVALID_ARG, "window and dilation must not be NULL");
   for (int h = 0; h < p->heads; ++h) {
     if (p->window[h] < 0 || (p->window[h] & 1))
@@ -160,6 +164,39 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
         }
     nband_blocks = (long)tiles.size();
   }
+  // Key split: with fewer band workgroups than half the CUs the forward is
+  // one short round of latency-bound workgroups; sharing each tile's keys
+  // over two workgroups (merged afterwards) then pays (the LED decoder's
+  // 96 tiles: 19.2 -> 17.2 us). Larger grids lose more to the partials'
+  // traffic and the merge than they gain (one 4096-token sequence, 384
+  // tiles: 19.8 -> 26.5 us), so they are not split unless asked.
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  int parts = p->key_split > 0 ? p->key_split : 1;
+  if (p->key_split == 0 && nband_blocks > 0 && 2 * nband_blocks < cus) {
+    double avg_tiles = 0;  // key tiles per band tile, on average
+    if (uniform) {
+      const int nr0 = (p->n + dil[0] - 1) / dil[0];
+      avg_tiles = std::min<double>((nr0 + KT - 1) / KT,
+                                   (double)(BM + half[0] + (p->causal ? 0 : half[0]) + KT - 1) / KT);
+    } else {
+      for (const TileRec& t : tiles) {
+        const int kb = std::max(0, t.q0 - t.half), ke = std::min(t.nr, t.q0 + BM + t.right);
+        avg_tiles += (double)((ke - kb + KT - 1) / KT);
+      }
+      avg_tiles /= (double)tiles.size();
+    }
+    if (avg_tiles >= 4) parts = 2;
+  }
+  const size_t split_bytes = parts > 1 ? (size_t)bh * p->n * parts * PART_STRIDE * sizeof(float) : 0;
+  if (split_bytes > ((size_t)1 << 30)) return fail(SWATTN_ERR_UNSUPPORTED, "key split workspace above 1 GiB");
+  if (nband_blocks * parts > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
+
   // the backward launch holds two blocks per band tile
   if (2 * nband_blocks > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
 
@@ -169,6 +206,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->causal = p->causal; pl->ng = ng_max; pl->dtype = p->dtype;
   pl->per_item = per_item && ng_max > 0;
   pl->nband_blocks = (int)nband_blocks;
+  pl->parts = parts;
+  pl->band_part = nullptr;
   pl->uni_half = half[0];
   pl->uni_right = p->causal ? 0 : half[0];
   pl->uni_dil = dil[0];
@@ -180,7 +219,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   if (pl->ng > 0) {
     choose_split(p->n, &pl->nsplit, &pl->ksplit);
     const long nglob = (long)pl->nsplit * pl->ngroup * bh;
-    if (nglob + nband_blocks > 0x7fffffffL) {
+    if (nglob + nband_blocks * parts > 0x7fffffffL) {
       delete pl;
       return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
     }
@@ -226,7 +265,9 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const size_t sz_gstat = al(sizeof(float) * (size_t)bh * pl->ngp);
   const size_t sz_gkv = al(sizeof(float) * (size_t)bh * pl->nchunk * pl->ng32 * 2 * HD);
   const size_t sz_heads = al(sizeof(HeadGeom) * p->heads);
-  const size_t total = sz_tiles + sz_g + sz_goff + sz_po + sz_pml + 2 * sz_stat + 2 * sz_gstat + sz_gkv + sz_heads;
+  const size_t sz_split = al(split_bytes);
+  const size_t total = sz_tiles + sz_g + sz_goff + sz_po + sz_pml + 2 * sz_stat + 2 * sz_gstat + sz_gkv + sz_heads +
+                       sz_split;
   e = hipMalloc(&pl->dev_mem, total);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
   char* m = static_cast<char*>(pl->dev_mem);
@@ -240,7 +281,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->bwd_glse2 = reinterpret_cast<float*>(m); m += sz_gstat;
   pl->bwd_gdd = reinterpret_cast<float*>(m); m += sz_gstat;
   pl->bwd_part_gkv = reinterpret_cast<float*>(m); m += sz_gkv;
-  pl->bwd_heads = reinterpret_cast<HeadGeom*>(m);
+  pl->bwd_heads = reinterpret_cast<HeadGeom*>(m); m += sz_heads;
+  pl->band_part = sz_split ? reinterpret_cast<float*>(m) : nullptr;
   e = hipSuccess;
   if (!tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
@@ -296,7 +338,7 @@ extern "C" int swattn_kernel_times(swattn_plan* pl, float* band_ms, float* globa
     float a = 0, b = 0;
     hipError_t e = hipEventSynchronize(pl->ev[4 * i + 1]);
     if (e == hipSuccess) e = hipEventElapsedTime(&a, pl->ev[4 * i + 0], pl->ev[4 * i + 1]);
-    if (e == hipSuccess && pl->ng > 0) {
+    if (e == hipSuccess && (pl->ng > 0 || pl->parts > 1)) {
       e = hipEventSynchronize(pl->ev[4 * i + 3]);
       if (e == hipSuccess) e = hipEventElapsedTime(&b, pl->ev[4 * i + 2], pl->ev[4 * i + 3]);
     }
@@ -339,6 +381,7 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   bp.tiles = pl->tiles; bp.gidx = pl->gidx; bp.goff = pl->goff; bp.ng = pl->ng;
   bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
   bp.uni_nqb = pl->uni_nqb;
+  bp.parts = pl->parts; bp.part = pl->band_part;
   bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   GlobalParams gp;
@@ -353,18 +396,35 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   hipEvent_t* ev = timed ? &pl->ev[4 * (size_t)pl->ntimed] : nullptr;
   if (timed) pl->ntimed++;
   // With timing on, the launches carry start/stop events that the runtime
-  // records at the kernel's own start and end (no event packets in between).
-  const dim3 grid(pl->nband_blocks + pl->nglob_blocks), block(256);
+  // records at the kernel's own start and end (no event packets in between):
+  // the forward kernel, and the merges after it (the key-split merge and the
+  // global-row merge, first start to last end).
+  const int nfwd = pl->nband_blocks * pl->parts;
+  const dim3 grid(nfwd + pl->nglob_blocks), block(256);
   if (timed)
-    hipExtLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, ev[0], ev[1], 0, bp, gp, pl->nband_blocks);
+    hipExtLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, ev[0], ev[1], 0, bp, gp, nfwd);
   else
-    hipLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, bp, gp, pl->nband_blocks);
+    hipLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, bp, gp, nfwd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch attn_fwd");
+  if (pl->parts > 1) {
+    // every row of O and LSE from its key parts (the rows of G are
+    // overwritten by the global-row merge after it)
+    const long rows = (long)pl->B * pl->H * pl->n;
+    const dim3 bgrid((unsigned)((rows + 15) / 16));
+    hipEvent_t stop = pl->ng > 0 ? nullptr : (timed ? ev[3] : nullptr);
+    if (timed)
+      hipExtLaunchKernelGGL(band_merge<T>, bgrid, block, 0, st, ev[2], stop, 0, bp, rows);
+    else
+      hipLaunchKernelGGL(band_merge<T>, bgrid, block, 0, st, bp, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch band_merge");
+  }
   if (pl->ng > 0) {
     const dim3 mgrid(pl->ng * pl->B * pl->H);
+    hipEvent_t start = pl->parts > 1 ? nullptr : (timed ? ev[2] : nullptr);
     if (timed)
-      hipExtLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, ev[2], ev[3], 0, gp);
+      hipExtLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, start, ev[3], 0, gp);
     else
       hipLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, gp);
     e = hipGetLastError();

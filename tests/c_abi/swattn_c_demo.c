@@ -50,6 +50,9 @@ static int validate(void) {
   p.d = 128;
   bad |= expect(swattn_create(&p, &plan), SWATTN_ERR_UNSUPPORTED, "d = 128");
   p.d = 64;
+  p.key_split = 17;
+  bad |= expect(swattn_create(&p, &plan), SWATTN_ERR_INVALID_ARG, "key_split 17");
+  p.key_split = 0;
   bad |= expect(swattn_create(NULL, &plan), SWATTN_ERR_INVALID_ARG, "NULL params");
   bad |= expect(swattn_forward(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL),
                 SWATTN_ERR_INVALID_ARG, "forward without a plan");

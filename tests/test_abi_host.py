@@ -41,7 +41,8 @@ def _params(**kw):
                         win, dil, kw.get("causal", 0),
                         ctypes.cast(G, ctypes.POINTER(ctypes.c_int32)),
                         kw.get("n_global", len(gl)), kw.get("dtype", 0),
-                        ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O is not None else None)
+                        ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O is not None else None,
+                        kw.get("key_split", 0))
     return p, (win, dil, G, O)
 
 
@@ -51,7 +52,7 @@ def _params(**kw):
     (dict(window=[3, 4]), 1), (dict(window=[-2, 4]), 1), (dict(dilation=[0, 1]), 1),
     (dict(global_idx=[3, 3]), 1), (dict(global_idx=[16]), 1),
     (dict(global_idx=[-1]), 1), (dict(n_global=17), 1), (dict(d=128), 2),
-    (dict(dtype=7), 2),
+    (dict(dtype=7), 2), (dict(key_split=-1), 1), (dict(key_split=17), 1),
     # per-example sets: offsets must start at 0, end at n_global, not decrease;
     # each item's set in [0, n), no repeats within an item, at most n entries
     (dict(batch=2, global_idx=[1, 2], offsets=[1, 1, 2]), 1),

@@ -112,3 +112,19 @@ def test_full_size_headline_all_seeds():
     wl = WORKLOADS["encoder_b2_h12_n4096_w512_g1"]
     for seed in (1, 2):
         _case(wl, seed, "sharp", rows=_sample_rows(wl, seed=seed))
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("key_split", [1, 3, 8])
+def test_key_split_forced(wl, key_split):
+    """The band keys of every tile shared out over 1 (no split), 3 or 8
+    workgroups, merged afterwards: the same result within the tolerances
+    (small problems otherwise choose their split themselves)."""
+    from sliding_window_attention_banded_amd import Plan
+    print(f"[parity] {wl.name} key_split={key_split}", flush=True)
+    inp = make_inputs(wl, 0, "sharp")
+    with Plan(wl.batch, wl.heads, wl.n, wl.d, wl.window, wl.dilation, wl.causal,
+              wl.global_idx, wl.torch_dtype, key_split=key_split) as pl:
+        o, lse = run_gpu(wl, inp, plan=pl)
+    ref_o, ref_lse = oracle_ref(wl, inp)
+    compare(wl, o, lse, ref_o, ref_lse, label=f"{wl.name}/split{key_split}")
