@@ -9,29 +9,41 @@
 // straight into out[p][b][h][i][0..63], the layout the attention reads, with
 // an optional bias added in fp32 before the bf16 rounding.
 //
-// Workgroup tile: 256 tokens x 128 features, 4 waves as 2 x 2, each wave
-// 128 tokens x 64 features = 4 x 2 MFMA 32x32x16 tiles. Both operands are
-// read k-contiguous (W rows and x rows), 32 input features per stage,
-// through a 3-stage LDS ring (72 KB) filled by direct global->LDS loads, so
-// that two workgroups share a CU and one's ring fill and stores run under
-// the other's MFMAs.
+// Workgroup tile: 128 tokens x 128 features, 4 waves as 2 x 2, each wave
+// 64 tokens x 64 features = 2 x 2 MFMA 32x32x16 tiles (the token count is a
+// template parameter, PjCfg). Both operands are read k-contiguous (W rows
+// and x rows), 32 input features per stage, through a 3-stage LDS ring
+// (48 KB) filled by direct global->LDS loads, so that three workgroups share
+// a CU and one's ring fill and stores run under the others' MFMAs.
 #pragma once
 
 #include "kernels.hpp"
 
 namespace swattn {
 
-constexpr int PJ_TM = 256;                                 // tokens per workgroup
 constexpr int PJ_TN = 128;                                 // output features per workgroup
 constexpr int PJ_TK = 32;                                  // input features per stage
 constexpr int PJ_ROWB = PJ_TK * 2;                         // bytes per staged row (bf16)
 constexpr int PJ_A_BYTES = PJ_TN * PJ_ROWB;                // W tile, 8 KB
-constexpr int PJ_STAGE_BYTES = PJ_A_BYTES + PJ_TM * PJ_ROWB;  // + x tile, 24 KB
-constexpr int PJ_NI = PJ_STAGE_BYTES / 1024;               // 1-KB loads per stage
-constexpr int PJ_PER_WAVE = PJ_NI / 4;                     // 6 per wave
-constexpr int PJ_A_NI = PJ_A_BYTES / 1024;                 // the first 8 fill the W tile
+constexpr int PJ_A_NI = PJ_A_BYTES / 1024;                 // the first 8 loads fill the W tile
 constexpr int PJ_RPB = 1024 / PJ_ROWB;                     // rows per 1-KB load
 constexpr int PJ_GROUP = 4;                                // token tiles swept together
+
+// Workgroup shapes: TG 32-token groups per wave, so 2 * 32 * TG tokens per
+// workgroup. The library launches TG = 2: 128 tokens, a 48 KB ring, three
+// workgroups per CU. TG = 4 (256 tokens, a 72 KB ring, two per CU, fewer
+// operand bytes per MFMA) ran within a few percent of it on the encoder,
+// QA, LED and AR-LM projections and 1.5x slower on small ones (1024 tokens:
+// 13.9 against 9.4 us), where its fewer, larger tiles leave CUs idle.
+template <int TG>
+struct PjCfg {
+  static constexpr int WT = 32 * TG;                       // tokens per wave
+  static constexpr int TM = 2 * WT;                        // tokens per workgroup
+  static constexpr int STAGE = PJ_A_BYTES + TM * PJ_ROWB;  // W + x tile per stage
+  static constexpr int NI = STAGE / 1024;                  // 1-KB loads per stage
+  static constexpr int PW = NI / 4;                        // loads per wave
+  static_assert(NI % 4 == 0, "loads split evenly over the four waves");
+};
 
 struct ProjParams {
   const __bf16* x;     // [M][D]
@@ -44,7 +56,8 @@ struct ProjParams {
   int n;
   int B;
   int H;
-  int ntm;             // ceil(M / 256)
+  int tg;              // workgroup shape (PjCfg)
+  int ntm;             // ceil(M / (64 * tg))
   int ntn;             // ceil(N / 128)
   int nblocks;         // ntm * ntn
 };
@@ -76,25 +89,27 @@ DEV void wait_lgkm0() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds[3 * PJ_STAGE_BYTES];
+template <int TG>
+__global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) {
+  using C = PjCfg<TG>;
+  __shared__ __attribute__((aligned(1024))) char lds[3 * C::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   pj_tile(blockIdx.x, p, tm, tn);
-  const int tok0 = tm * PJ_TM, feat0 = tn * PJ_TN;
+  const int tok0 = tm * C::TM, feat0 = tn * PJ_TN;
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)lds;
   const unsigned rowbytes = (unsigned)p.D * 2u;
 
   // Load lane offsets: load I of a stage fills LDS rows 16*(I mod 8) .. +15
   // of the W tile (I < 8) or of the x tile; lane L writes the 16-byte slot
   // L of the 1-KB block, which holds logical chunk pj_phys(row, L % 4).
-  unsigned doff[PJ_PER_WAVE];
+  unsigned doff[C::PW];
 #pragma unroll
-  for (int i = 0; i < PJ_PER_WAVE; ++i) {
-    const int I = wave * PJ_PER_WAVE + i;
+  for (int i = 0; i < C::PW; ++i) {
+    const int I = wave * C::PW + i;
     const bool is_w = I < PJ_A_NI;
     const int row = (is_w ? I : I - PJ_A_NI) * PJ_RPB + (lane >> 2);
     const int grow = is_w ? min(feat0 + row, p.N - 1) : min(tok0 + row, p.M - 1);
@@ -104,10 +119,10 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
     const char* wb = reinterpret_cast<const char*>(p.w) + (size_t)step * PJ_ROWB;
     const char* xb = reinterpret_cast<const char*>(p.x) + (size_t)step * PJ_ROWB;
 #pragma unroll
-    for (int i = 0; i < PJ_PER_WAVE; ++i) {
-      const int I = wave * PJ_PER_WAVE + i;
+    for (int i = 0; i < C::PW; ++i) {
+      const int I = wave * C::PW + i;
       dma16_saddr(I < PJ_A_NI ? wb : xb, doff[i],
-                  lds0 + (unsigned)(stage * PJ_STAGE_BYTES + I * 1024));
+                  lds0 + (unsigned)(stage * C::STAGE + I * 1024));
     }
   };
 
@@ -119,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
   for (int ks = 0; ks < 2; ++ks) roff[ks] = pj_off(lane & 31, 2 * ks + (lane >> 5));
   const int wm = wave >> 1, wn = wave & 1;
   const int a_off = wn * 64 * PJ_ROWB;                // this wave's 64 W rows
-  const int b_off = PJ_A_BYTES + wm * 128 * PJ_ROWB;  // this wave's 128 x rows
+  const int b_off = PJ_A_BYTES + wm * C::WT * PJ_ROWB;  // this wave's x rows
 
   // This wave's 64 output features are one (projection, head) block; its
   // bias is read before the main loop so that the load's latency is hidden.
@@ -136,27 +151,27 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
         bq[f][jq] = *reinterpret_cast<const bf16x4*>(p.bias + ph * 64 + f * 32 + 8 * jq + 4 * g);
     }
 
-  f32x16 acc[2][4];
+  f32x16 acc[2][TG];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TG; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[f][t][r] = 0.f;
 
-  auto read_frags = [&](const char* sb, int ks, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
+  auto read_frags = [&](const char* sb, int ks, bf16x8 (&a)[2], bf16x8 (&b)[TG]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f)
       a[f] = *reinterpret_cast<const bf16x8*>(sb + a_off + f * 32 * PJ_ROWB + roff[ks]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TG; ++t)
       b[t] = *reinterpret_cast<const bf16x8*>(sb + b_off + t * 32 * PJ_ROWB + roff[ks]);
   };
-  // MFMAs k0 .. k1-1 of one 16-feature step, k = 4 * (feature group) + token group
-  auto mma = [&](const bf16x8 (&a)[2], const bf16x8 (&b)[4], int k0, int k1) {
+  // MFMAs k0 .. k1-1 of one 16-feature step, k = TG * (feature group) + token group
+  auto mma = [&](const bf16x8 (&a)[2], const bf16x8 (&b)[TG], int k0, int k1) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k >= k0 && k < k1) acc[k / 4][k % 4] = mfma_bf16(a[k / 4], b[k % 4], acc[k / 4][k % 4]);
+    for (int k = 0; k < 2 * TG; ++k)
+      if (k >= k0 && k < k1) acc[k / TG][k % TG] = mfma_bf16(a[k / TG], b[k % TG], acc[k / TG][k % TG]);
   };
 
   // Ring: stage s % 3 holds input features 32s .. 32s+31. Per stage: the
@@ -168,44 +183,44 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
   const int nk = p.D / PJ_TK;
   issue(0, 0);
   if (nk > 1) issue(1, 1);
-  if (nk > 1) wait_vmcnt<PJ_PER_WAVE>();
+  if (nk > 1) wait_vmcnt<C::PW>();
   else wait_vmcnt<0>();
   wg_barrier();  // stage 0 has landed for every wave
   if (nk > 2) issue(2, 2);
-  bf16x8 a0[2], b0[4], a1[2], b1[4];
+  bf16x8 a0[2], b0[TG], a1[2], b1[TG];
   read_frags(lds, 0, a0, b0);
   int stage = 0;
   for (int s = 0; s + 1 < nk; ++s) {
-    const char* sb = lds + stage * PJ_STAGE_BYTES;
+    const char* sb = lds + stage * C::STAGE;
     const int nstage = stage == 2 ? 0 : stage + 1;
     read_frags(sb, 1, a1, b1);
-    mma(a0, b0, 0, 8);
-    if (s + 2 < nk) wait_vmcnt<PJ_PER_WAVE>();
+    mma(a0, b0, 0, 2 * TG);
+    if (s + 2 < nk) wait_vmcnt<C::PW>();
     else wait_vmcnt<0>();
     wait_lgkm0();  // this wave's reads of stage s have returned
     wg_barrier();  // stage s+1 has landed for every wave; stage s is consumed
-    mma(a1, b1, 0, 4);
+    mma(a1, b1, 0, TG);
     if (s + 3 < nk) issue(s + 3, stage);
-    read_frags(lds + nstage * PJ_STAGE_BYTES, 0, a0, b0);
-    mma(a1, b1, 4, 8);
+    read_frags(lds + nstage * C::STAGE, 0, a0, b0);
+    mma(a1, b1, TG, 2 * TG);
     stage = nstage;
   }
-  read_frags(lds + stage * PJ_STAGE_BYTES, 1, a1, b1);
-  mma(a0, b0, 0, 8);
-  mma(a1, b1, 0, 8);
+  read_frags(lds + stage * C::STAGE, 1, a1, b1);
+  mma(a0, b0, 0, 2 * TG);
+  mma(a1, b1, 0, 2 * TG);
 
   // Epilogue. Lane l holds token column l % 32 of each 32-token group and,
   // in register j, feature 8*(j/4) + 4*(l/32) + j%4 of each 32-feature group.
-  // Each wave stages its 128 x 64 tile (bias added, rounded to bf16) in its
-  // own 16 KB of the ring as [token][64 features], 8-byte unit u of row r at
+  // Each wave stages its WT x 64 tile (bias added, rounded to bf16) in its
+  // own WT * 128 bytes of the ring as [token][64 features], 8-byte unit u of row r at
   // u ^ ((r >> 1) & 15) (conflict-free for both access patterns), then
   // writes whole 128-byte token rows: 8 rows per store instruction.
   wait_lgkm0();
   wg_barrier();  // every wave is done with the ring
   if (!ph_ok) return;
-  char* st = lds + wave * (128 * 128);
+  char* st = lds + wave * (C::WT * 128);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < TG; ++t) {
     const int row = t * 32 + (lane & 31);
     const int k = (row >> 1) & 15;
 #pragma unroll
@@ -221,30 +236,30 @@ __global__ __launch_bounds__(256, 2) void proj_gemm(ProjParams p) {
   }
   wait_lgkm0();  // the wave reads back what its other lanes wrote
   const int proj = ph / p.H, h = ph - proj * p.H;
-  const int T = tok0 + wm * 128;  // this wave's first token
+  const int T = tok0 + wm * C::WT;  // this wave's first token
   __bf16* obase = p.out + ((size_t)proj * p.B * p.H + h) * (size_t)p.n * 64;
   const size_t item_stride = (size_t)p.H * p.n * 64;
   const int item0 = T / p.n, pos0 = T - item0 * p.n;
-  const bool one_item = pos0 + 128 <= p.n;  // wave-uniform
-  if (one_item && T + 128 <= p.M) {
-    // every row exists and the 128 rows are consecutive in out: read the
+  const bool one_item = pos0 + C::WT <= p.n;  // wave-uniform
+  if (one_item && T + C::WT <= p.M) {
+    // every row exists and the wave's rows are consecutive in out: read the
     // whole tile back first, then store it without per-lane conditions
     __bf16* orow = obase + item0 * item_stride + (size_t)pos0 * 64;
-    uint4 v[16];
+    uint4 v[C::WT / 8];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < C::WT / 8; ++it) {
       const int row = it * 8 + (lane >> 3), c = lane & 7;
       const int k = (row >> 1) & 15;
       v[it] = *reinterpret_cast<const uint4*>(st + row * 128 + ((c ^ (k >> 1)) << 4));
       if (k & 1) v[it] = uint4{v[it].z, v[it].w, v[it].x, v[it].y};
     }
 #pragma unroll
-    for (int it = 0; it < 16; ++it)
+    for (int it = 0; it < C::WT / 8; ++it)
       *reinterpret_cast<uint4*>(orow + (size_t)(it * 8 + (lane >> 3)) * 64 + (lane & 7) * 8) = v[it];
     return;
   }
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
+  for (int it = 0; it < C::WT / 8; ++it) {
     const int row = it * 8 + (lane >> 3), c = lane & 7;
     const int k = (row >> 1) & 15;
     uint4 v = *reinterpret_cast<const uint4*>(st + row * 128 + ((c ^ (k >> 1)) << 4));

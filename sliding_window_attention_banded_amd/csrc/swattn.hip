@@ -546,7 +546,9 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   const size_t xb = (size_t)M * d_model * 2, wb = (size_t)N * d_model * 2, ob = (size_t)M * N * 2;
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, bias, (size_t)N * 2))
     return fail(SWATTN_ERR_INVALID_ARG, "out overlaps an input");
-  const long ntm = (M + PJ_TM - 1) / PJ_TM, ntn = (N + PJ_TN - 1) / PJ_TN;
+  constexpr int tg = 2;  // workgroup shape (PjCfg)
+  const long tm_tokens = 64L * tg;
+  const long ntm = (M + tm_tokens - 1) / tm_tokens, ntn = (N + PJ_TN - 1) / PJ_TN;
   if (ntm * ntn > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
   ProjParams pp;
   pp.x = static_cast<const __bf16*>(x);
@@ -554,8 +556,8 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   pp.bias = static_cast<const __bf16*>(bias);
   pp.out = static_cast<__bf16*>(out);
   pp.M = (int)M; pp.N = (int)N; pp.D = d_model; pp.n = n; pp.B = batch; pp.H = heads;
-  pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn);
-  hipLaunchKernelGGL(proj_gemm, dim3((unsigned)pp.nblocks), dim3(256), 0,
+  pp.tg = tg; pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn);
+  hipLaunchKernelGGL(proj_gemm<tg>, dim3((unsigned)pp.nblocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), pp);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch proj_gemm");
