@@ -9,12 +9,12 @@
 // straight into out[p][b][h][i][0..63], the layout the attention reads, with
 // an optional bias added in fp32 before the bf16 rounding.
 //
-// Workgroup tile: 128 tokens x 128 features, 4 waves as 2 x 2, each wave
-// 64 tokens x 64 features = 2 x 2 MFMA 32x32x16 tiles (the token count is a
-// template parameter, PjCfg). Both operands are read k-contiguous (W rows
-// and x rows), 32 input features per stage, through a 3-stage LDS ring
-// (48 KB) filled by direct global->LDS loads, so that three workgroups share
-// a CU and one's ring fill and stores run under the others' MFMAs.
+// Workgroup tile: 256 (or 128) tokens x 128 features, 4 waves as 2 x 2, each
+// wave 128 (64) tokens x 64 features = 4 (2) x 2 MFMA 32x32x16 tiles (PjCfg).
+// Both operands are read k-contiguous (W rows and x rows), 32 input features
+// per stage, through a 3-stage LDS ring filled by direct global->LDS loads,
+// so that two (three) workgroups share a CU and one's ring fill and stores
+// run under the others' MFMAs.
 #pragma once
 
 #include "kernels.hpp"
@@ -30,11 +30,11 @@ constexpr int PJ_RPB = 1024 / PJ_ROWB;                     // rows per 1-KB load
 constexpr int PJ_GROUP = 4;                                // token tiles swept together
 
 // Workgroup shapes: TG 32-token groups per wave, so 2 * 32 * TG tokens per
-// workgroup. The library launches TG = 2: 128 tokens, a 48 KB ring, three
-// workgroups per CU. TG = 4 (256 tokens, a 72 KB ring, two per CU, fewer
-// operand bytes per MFMA) ran within a few percent of it on the encoder,
-// QA, LED and AR-LM projections and 1.5x slower on small ones (1024 tokens:
-// 13.9 against 9.4 us), where its fewer, larger tiles leave CUs idle.
+// workgroup. TG = 4: 256 tokens, a 72 KB ring, two workgroups per CU, fewer
+// operand bytes per MFMA (the encoder projection: 79 us against 88 us with
+// TG = 2). TG = 2: 128 tokens, a 48 KB ring, three per CU, for problems whose
+// 256-token tiles cannot give every CU two workgroups (1024 tokens: 9.4 us
+// against 13.9 us).
 template <int TG>
 struct PjCfg {
   static constexpr int WT = 32 * TG;                       // tokens per wave
@@ -78,6 +78,11 @@ DEV void pj_tile(int bid, const ProjParams& p, int& tm, int& tn) {
   const int gm = min(PJ_GROUP, p.ntm - grp * PJ_GROUP);
   tn = r / gm;
   tm = grp * PJ_GROUP + (r - tn * gm);
+}
+
+inline int proj_choose_tg(long M, long N, int cus) {
+  const long big_tiles = (M + 255) / 256 * ((N + PJ_TN - 1) / PJ_TN);
+  return big_tiles < 2L * cus ? 2 : 4;
 }
 
 // Wait until this wave's LDS reads have returned (their registers are

@@ -546,7 +546,14 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   const size_t xb = (size_t)M * d_model * 2, wb = (size_t)N * d_model * 2, ob = (size_t)M * N * 2;
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, bias, (size_t)N * 2))
     return fail(SWATTN_ERR_INVALID_ARG, "out overlaps an input");
-  constexpr int tg = 2;  // workgroup shape (PjCfg)
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  const int tg = proj_choose_tg(M, N, cus);  // workgroup shape (PjCfg)
   const long tm_tokens = 64L * tg;
   const long ntm = (M + tm_tokens - 1) / tm_tokens, ntn = (N + PJ_TN - 1) / PJ_TN;
   if (ntm * ntn > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
@@ -557,8 +564,12 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   pp.out = static_cast<__bf16*>(out);
   pp.M = (int)M; pp.N = (int)N; pp.D = d_model; pp.n = n; pp.B = batch; pp.H = heads;
   pp.tg = tg; pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn);
-  hipLaunchKernelGGL(proj_gemm<tg>, dim3((unsigned)pp.nblocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), pp);
+  if (tg == 4)
+    hipLaunchKernelGGL(proj_gemm<4>, dim3((unsigned)pp.nblocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), pp);
+  else
+    hipLaunchKernelGGL(proj_gemm<2>, dim3((unsigned)pp.nblocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), pp);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch proj_gemm");
   return SWATTN_OK;
