@@ -174,7 +174,7 @@ def main():
             step(i)
         band_ms, glob_ms, cnt = plan.kernel_times()
         plan.set_timing(False)
-        print(f"[bench] forward kernel {band_ms * 1e3:.2f} us, global-row merge "
+        print(f"[bench] forward kernel {band_ms * 1e3:.2f} us, merges after it "
               f"{glob_ms * 1e3:.2f} us (HIP events, {cnt} launches)", file=sys.stderr, flush=True)
 
     bf = band_flops(wl)
