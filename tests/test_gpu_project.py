@@ -118,3 +118,42 @@ def test_project_rejects_fp32_and_bad_shapes():
         project(x, w, heads=1)
     with pytest.raises(SwattnError):
         project(x.bfloat16(), torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda"), heads=1)
+
+
+def _draw(i):
+    rng = np.random.default_rng(500 + i)
+    B = int(rng.integers(1, 4))
+    n = int(rng.integers(1, 40)) if rng.random() < 0.2 else int(rng.integers(40, 1500))
+    D = 32 * int(rng.integers(1, 33))        # any multiple of 32 up to 1024
+    H = int(rng.integers(1, 7))
+    P = int(rng.integers(1, 7))
+    return B, n, D, H, P, bool(rng.random() < 0.7)
+
+
+def _draw_large(i):
+    # large enough for 256-token workgroups (at least two per CU), ragged
+    rng = np.random.default_rng(900 + i)
+    B = int(rng.integers(1, 4))
+    n = int(rng.integers(8000, 20001)) // B | 1
+    D = int(rng.choice([512, 768]))
+    H = int(rng.integers(4, 13))
+    P = int(rng.integers(3, 7))
+    return B, n, D, H, P, bool(rng.random() < 0.7)
+
+
+RANDOM = [_draw(i) for i in range(32)] + [_draw_large(i) for i in range(4)]
+
+
+@pytest.mark.parametrize("B,n,D,H,P,bias", RANDOM,
+                         ids=[f"r{i}_B{c[0]}_n{c[1]}_D{c[2]}_H{c[3]}_P{c[4]}" for i, c in enumerate(RANDOM)])
+def test_project_random_shapes(B, n, D, H, P, bias):
+    """Seeded shapes: batch, ragged token counts (1 to 1500, and four large
+    ones of 8000 to 20000 tokens), d_model any multiple of 32 up to 1024, 1
+    to 12 heads, 1 to 6 projections, with or without bias; the small ones
+    run 128-token workgroups, the large ones 256-token workgroups."""
+    from sliding_window_attention_banded_amd import project
+    print(f"[proj] random B{B} n{n} D{D} H{H} P{P} bias={bias}", flush=True)
+    x, w, b = make_projection_inputs(B, n, D, H, P, 11, bias)
+    out = project(x.cuda(), w.cuda(), b.cuda() if b is not None else None, heads=H)
+    torch.cuda.synchronize()
+    _check(out, x, w, b, H, f"rand B{B}n{n}D{D}H{H}P{P}")
