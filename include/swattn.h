@@ -80,14 +80,18 @@ typedef struct swattn_plan swattn_plan;
 
 /*
  * Validate the parameters and build a plan: per-head (left, right, dilation)
- * table, the residue-class tile schedule of the band, the sorted device copy
- * of G, and the device workspace for the global-row pass. Every host array is
- * copied; the caller may free them when this returns. Uses the current HIP
- * device; the plan may only be used with streams of that device.
+ * table, the residue-class tile schedule of the band and its key split, the
+ * sorted device copy of G (per item with global_offsets), and one device
+ * allocation for every workspace the forward and backward use (global-row
+ * partials, key-split partials, the backward's per-row statistics). Every
+ * host array is copied; the caller may free them when this returns. Uses the
+ * current HIP device; the plan may only be used with streams of that device.
  * On success *out receives the plan; on failure *out is untouched.
  * Errors: INVALID_ARG (null pointers, ranges, odd window, dilation < 1,
- * repeated or out-of-range global index), UNSUPPORTED (d != 64, unknown
- * dtype), HIP (device allocation or copy failed; see swattn_last_error()).
+ * repeated or out-of-range global index, bad global_offsets, key_split
+ * outside [0, 16]), UNSUPPORTED (d != 64, unknown dtype, sizes beyond the
+ * 32-bit grid limits or a key-split workspace above 1 GiB), HIP (device
+ * allocation or copy failed; see swattn_last_error()).
  */
 int swattn_create(const swattn_params* p, swattn_plan** out);
 
