@@ -6,7 +6,8 @@ pass, merge) over one batch of the workload, inputs already resident in HBM.
 Prints ONE JSON line. The throughput `value` is band TFLOP/s (4*d*sum of
 window keys per row, the closed form of the Longformer window), measured over
 K steps that rotate through enough input sets to exceed the 256 MB Infinity
-Cache; the warm (single input set) figure is reported beside it. The same
+Cache; the warm (single input set) figure, the median of 10 samples of K
+steps, is reported beside it. The same
 line carries the backward pass of the workload ("backward") and the
 projections in front of it ("projection": Q, K, V and, with global tokens,
 Qg, Kg, Vg from an input of d_model = heads*64 features), each timed the
@@ -89,7 +90,21 @@ def cpu_baseline(wl, seconds):
                   f"{dt:.1f} s",
         "tokens_per_s": done_rows / wl.heads / dt,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
+        "blas": sorted({x.get("internal_api", "?") for x in threadpool_info()
+                        if x.get("user_api") == "blas"}),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -162,7 +177,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     ms = timed(args.steps, rotate=True)          # the headline: rotating sets
-    ms_warm = timed(args.steps, rotate=False)    # one input set, cache-warm
+    # one input set, cache-warm: the median of 10 samples of K steps
+    warm_samples = sorted(timed(args.steps, rotate=False) for _ in range(10))
+    ms_warm = 0.5 * (warm_samples[4] + warm_samples[5])
     print(f"[bench] {ms * 1e3:.2f} us/step (rotating), {ms_warm * 1e3:.2f} us/step (warm)",
           file=sys.stderr, flush=True)
 
@@ -311,7 +328,8 @@ def main():
         "useful_tflops": useful_flops(wl) / (ms * 1e-3) / 1e12,
         "algorithmic_gbs": algorithmic_bytes(wl) / (ms * 1e-3) / 1e9,
         "warm": {"ms_per_step": ms_warm, "value": bf / (ms_warm * 1e-3) / 1e12,
-                 "tokens_per_s": tokens / (ms_warm * 1e-3)},
+                 "tokens_per_s": tokens / (ms_warm * 1e-3), "samples": 10,
+                 "ms_per_step_min": warm_samples[0], "ms_per_step_max": warm_samples[-1]},
         "input_sets": nsets,
         "roofline": roof,
         "backward": bwd,
