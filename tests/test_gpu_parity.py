@@ -45,6 +45,12 @@ SMALL = [
     # more than a 64-key tile)
     W("per_item", 3, 2, 700, (64, 16), (1, 3), False, ((0, 5, 699), (), tuple(range(100, 190)))),
     W("per_item_causal", 2, 3, 500, (32, 256, 2), (1, 4, 1), True, ((7,), (0, 250, 499))),
+    # one global token per item (the headline's and LED's case)
+    W("one_global", 2, 3, 1000, (64, 128, 30), (1, 2, 3), False, (17,)),
+    W("one_global_causal", 1, 4, 777, (32, 256, 2, 1024), (1, 4, 1, 2), True, (300,)),
+    W("one_global_fp32", 2, 3, 1000, (64, 128, 30), (1, 2, 3), False, (999,), "fp32"),
+    W("one_global_per_item", 3, 2, 700, (64, 16), (1, 3), False, ((5,), (), (699,))),
+    W("one_global_per_item_causal", 2, 2, 2100, (32, 256), (1, 4), True, ((0,), (2050,))),
 ]
 
 EDGE_N = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255]
@@ -128,3 +134,46 @@ def test_key_split_forced(wl, key_split):
         o, lse = run_gpu(wl, inp, plan=pl)
     ref_o, ref_lse = oracle_ref(wl, inp)
     compare(wl, o, lse, ref_o, ref_lse, label=f"{wl.name}/split{key_split}")
+
+
+@pytest.mark.parametrize("G", [(0,), ((3,), (), (1500,))], ids=["shared", "per_item"])
+def test_repeated_launches_one_global(G):
+    """Back-to-back forwards on one plan, each checked: every launch reuses
+    the plan's global-row workspace (the chunk partials and their merge), so
+    nothing a launch leaves there may leak into the next one."""
+    wl = W("repeat_one_global", 3 if len(G) == 3 else 2, 3, 1600, (64, 128, 30), (1, 2, 3),
+           False, G)
+    from sliding_window_attention_banded_amd import Plan
+    print(f"[parity] {wl.name} G={G}: 6 launches on one plan", flush=True)
+    with Plan(wl.batch, wl.heads, wl.n, wl.d, wl.window, wl.dilation, wl.causal,
+              wl.global_idx, wl.torch_dtype, key_split=1) as pl:
+        ins, outs = [], []
+        for seed in range(6):
+            inp = make_inputs(wl, 100 + seed, "sharp" if seed % 2 else "normal")
+            dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+            outs.append(pl.forward(dev["q"], dev["k"], dev["v"], dev["qg"], dev["kg"],
+                                   dev["vg"], want_lse=True))
+            ins.append(inp)
+        torch.cuda.synchronize()
+        for seed, (inp, (o, lse)) in enumerate(zip(ins, outs)):
+            ref_o, ref_lse = oracle_ref(wl, inp)
+            compare(wl, o.cpu(), lse.cpu(), ref_o, ref_lse, label=f"launch {seed}")
+
+
+ONE_GLOBAL = [w for w in SMALL if w.name.startswith("one_global")]
+
+
+@pytest.mark.parametrize("wl", ONE_GLOBAL, ids=lambda w: w.name)
+@pytest.mark.parametrize("kind", ["normal", "sharp"])
+def test_one_global_no_key_split(wl, kind):
+    """One global token and no key split (the headline's launch
+    configuration), whatever split the plan would choose for these shapes."""
+    from sliding_window_attention_banded_amd import Plan
+    with Plan(wl.batch, wl.heads, wl.n, wl.d, wl.window, wl.dilation, wl.causal,
+              wl.global_idx, wl.torch_dtype, key_split=1) as pl:
+        for seed in (0, 1):
+            print(f"[parity] {wl.name} key_split=1 seed={seed} kind={kind}", flush=True)
+            inp = make_inputs(wl, seed, kind)
+            o, lse = run_gpu(wl, inp, plan=pl)
+            ref_o, ref_lse = oracle_ref(wl, inp)
+            compare(wl, o, lse, ref_o, ref_lse, label=wl.name)
