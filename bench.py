@@ -11,7 +11,9 @@ steps, is reported beside it. The same
 line carries the backward pass of the workload ("backward") and the
 projections in front of it ("projection": Q, K, V and, with global tokens,
 Qg, Kg, Vg from an input of d_model = heads*64 features), each timed the
-same way.
+same way. "cpu_baseline" times the float64 oracle (the explicit n x n form)
+on the host cores over a bounded sample of the workload, and beside it
+("banded") the same definition evaluated band block by band block.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -93,7 +95,42 @@ def cpu_baseline(wl, seconds):
         "cpu_model": _cpu_model(),
         "blas": sorted({x.get("internal_api", "?") for x in threadpool_info()
                         if x.get("user_api") == "blas"}),
+        "banded": _cpu_banded(wl, f64, seconds / 2),
     }
+
+
+def _cpu_banded(wl, f64, seconds):
+    """The same definition evaluated over each row's enumerated keys
+    (oracle.attention_banded, O(n*w*d) float64), on whole (batch, head)
+    slices until `seconds` have passed: the CPU cost of the method itself,
+    beside the explicit n x n form above."""
+    from oracle import attention_banded
+    from sliding_window_attention_banded_amd.accounting import band_keys_per_row
+    from sliding_window_attention_banded_amd.workloads import item_globals
+
+    done_flops, done_rows, pairs = 0, 0, 0
+    t0 = time.perf_counter()
+    for b in range(wl.batch):
+        for h in range(wl.heads):
+            sl = lambda t: None if t is None else t[b:b + 1, h:h + 1]
+            attention_banded(sl(f64["q"]), sl(f64["k"]), sl(f64["v"]), sl(f64["qg"]),
+                             sl(f64["kg"]), sl(f64["vg"]), window=wl.window[h],
+                             dilation=wl.dilation[h], causal=wl.causal,
+                             global_idx=list(item_globals(wl)[b]))
+            done_flops += 4 * wl.d * int(band_keys_per_row(wl.n, wl.window[h],
+                                                           wl.dilation[h], wl.causal).sum())
+            done_rows += wl.n
+            pairs += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s",
+            "tokens_per_s": done_rows / wl.heads / dt,
+            "sample": f"{pairs} of {wl.batch * wl.heads} (batch, head) slices, all {wl.n} rows "
+                      f"each, float64 over each row's enumerated keys (NumPy), {dt:.1f} s"}
 
 
 def _cpu_model():

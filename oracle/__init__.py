@@ -12,7 +12,9 @@ and section 7 "Longformer-Encoder-Decoder" for the left-only (causal) mask.
 Every reading taken where the page is silent is listed in ``masked_softmax.py``.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against brute
-force, closed forms, library reductions and hand-derived golden values.
+force, closed forms, library reductions and hand-derived golden values;
+``attention_banded`` (the same definition over each row's enumerated keys,
+O(n*w*d)) is pinned against those pinned functions and brute force.
 """
 
 from .masked_softmax import (  # noqa: F401
@@ -22,4 +24,5 @@ from .masked_softmax import (  # noqa: F401
     band_mask,
     global_row_mask,
 )
+from .banded import attention_banded  # noqa: F401
 from .projection import project  # noqa: F401
