@@ -100,8 +100,8 @@ def cpu_baseline(wl, seconds):
 
 
 def _cpu_banded(wl, f64, seconds):
-    """The same definition evaluated over each row's enumerated keys
-    (oracle.attention_banded, O(n*w*d) float64), on whole (batch, head)
+    """The same definition evaluated band block by band block
+    (oracle.attention_banded, O(n*(w+R)*d) float64), on whole (batch, head)
     slices until `seconds` have passed: the CPU cost of the method itself,
     beside the explicit n x n form above."""
     from oracle import attention_banded
@@ -130,7 +130,8 @@ def _cpu_banded(wl, f64, seconds):
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s",
             "tokens_per_s": done_rows / wl.heads / dt,
             "sample": f"{pairs} of {wl.batch * wl.heads} (batch, head) slices, all {wl.n} rows "
-                      f"each, float64 over each row's enumerated keys (NumPy), {dt:.1f} s"}
+                      f"each, float64 band blocks of 128 rows per residue class against their band span "
+                      f"plus the global columns (NumPy + BLAS), {dt:.1f} s"}
 
 
 def _cpu_model():
