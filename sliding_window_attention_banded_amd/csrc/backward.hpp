@@ -679,6 +679,16 @@ struct GcolPol {
   }
   DEV bool interior(int) const { return false; }
   template <class T> DEV void mask(f32x16& t, int ku, int g) const {
+    if (dil == 1) {  // wave-uniform: no remainder to test
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qi = ku + key_of_reg<T>(j, g);  // query position
+        const int dl = qi - gpos;
+        const bool inband = dl >= -right && dl <= half;
+        if ((causal && gpos > qi) || inband || qi >= qend) t[j] = -__builtin_inff();
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int qi = ku + key_of_reg<T>(j, g);  // query position
