@@ -12,11 +12,10 @@
 //
 // Kernels:
 //  * bwd_prep: D_i and the log2-domain LSE (+inf on rows of G), per row; the
-//    same statistics of the global rows in a padded [BH][ngp] table; zeros
-//    for the rows of dqg off G.
+//    same statistics of the global rows in a padded [BH][ngp] table.
 //  * bwd_main, band query blocks: 128 query rows of one residue class, Q and
 //    dO in registers, key tiles (K, V) through the ring, the global-column
-//    tile first: dq = s dS K.
+//    tile first: dq = s dS K; and the zero rows of dqg off G.
 //  * bwd_main, band key blocks: 128 keys of one residue class, K and V in
 //    registers, query tiles (Q, dO, log2-LSE, D) through the ring: dk, dv.
 //  * bwd_main, global-row query blocks: rows of G (Qg, dO) against a chunk of
@@ -131,18 +130,6 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
       p.glse2[bh * p.ngp + lo] = p.lse[row] * LOG2E;
       p.gdd[bh * p.ngp + lo] = acc;
     }
-  }
-  // rows of dqg off G are zero (the rows of G come from the reduction)
-  if (row < rows && p.dqg) {
-    const int i = (int)(row % p.n);
-    int lo = 0, hi = gs.n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (gs.idx[mid] < i) lo = mid + 1;
-      else hi = mid;
-    }
-    if (!(lo < gs.n && gs.idx[lo] == i))
-      *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(p.dqg) + row * HD + 8 * part) = uint4{0, 0, 0, 0};
   }
 }
 
@@ -352,8 +339,17 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   }
   wait_vmcnt<0>();
 
-  if (wave_live && row_ok)
+  if (wave_live && row_ok) {
     store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dq) + roff), w.dq, p.scale, g);
+    // dQg is zero off G (rows of G, log2-LSE +inf, come from bwd_gred)
+    if (p.dqg && w.lse2 != __builtin_inff()) {
+      __bf16* zrow = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dqg) + roff);
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) *reinterpret_cast<uint2*>(zrow + 32 * dh + 8 * a + 4 * g) = uint2{0, 0};
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
