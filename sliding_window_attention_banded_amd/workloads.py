@@ -172,6 +172,28 @@ def make_inputs(wl: Workload, seed: int, kind: str = "normal"):
     return out
 
 
+def make_device_inputs(wl: Workload, seed: int, device):
+    """The "sharp" distribution of make_inputs (q, k ~ N(0,1) * 2, v ~ U(-1, 1);
+    qg, kg, vg likewise when the workload has global tokens), drawn directly
+    on ``device`` with its own seeded generator: for shapes too large to draw
+    on the host (several GB per tensor). Rounded to nearest-even into the
+    workload dtype."""
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    shape = (wl.batch, wl.heads, wl.n, wl.d)
+    out = {}
+    roles = ["q", "k", "v"] + (["qg", "kg", "vg"] if has_globals(wl) else [])
+    for r in roles:
+        if r in ("v", "vg"):
+            t = torch.rand(shape, generator=gen, device=device, dtype=torch.float32) * 2.0 - 1.0
+        else:
+            t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * 2.0
+        out[r] = t.to(wl.torch_dtype)
+        del t
+    for r in ("qg", "kg", "vg"):
+        out.setdefault(r, None)
+    return out
+
+
 def make_projection_inputs(batch, n, d_model, heads, nproj, seed, bias=True):
     """Seeded CPU bf16 tensors for the projections in front of the attention:
     x [batch, n, d_model] ~ N(0, 1) (a normalised layer input), weight

@@ -177,3 +177,31 @@ def test_one_global_no_key_split(wl, kind):
             o, lse = run_gpu(wl, inp, plan=pl)
             ref_o, ref_lse = oracle_ref(wl, inp)
             compare(wl, o, lse, ref_o, ref_lse, label=wl.name)
+
+
+def test_tensors_past_two_gib():
+    """Every [B, H, n, 64] tensor larger than 2 GiB (18 heads of 2^20 + 3
+    tokens): rows of the first and of the last head (whose data lies past
+    2^31 bytes), band rows near both ends, the global rows and random rows,
+    against the oracle on that head alone."""
+    from sliding_window_attention_banded_amd import Plan
+    from sliding_window_attention_banded_amd.workloads import make_device_inputs
+    n, H = (1 << 20) + 3, 18
+    wl = W("past_2gib", 1, H, n, 64, [1] * 16 + [3, 1], False, (7, n - 1))
+    assert H * n * 64 * 2 > (1 << 31)
+    print(f"[parity] {wl.name} B1 H{H} n{n} (sharp, drawn on the device)", flush=True)
+    dev = make_device_inputs(wl, 5, "cuda")
+    with Plan(wl.batch, wl.heads, wl.n, wl.d, wl.window, wl.dilation, wl.causal,
+              wl.global_idx, wl.torch_dtype) as pl:
+        o, lse = pl.forward(dev["q"], dev["k"], dev["v"], dev["qg"], dev["kg"], dev["vg"],
+                            want_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.array(sorted({0, 1, 7, 40, n // 2, n - 40, n - 2, n - 1}
+                           | set(rng.integers(0, n, 6).tolist())))
+    for h in (0, H - 2, H - 1):
+        one = W("past_2gib_head", 1, 1, n, wl.window[h], wl.dilation[h], False, (7, n - 1))
+        inp = {k: (v[:, h:h + 1].cpu() if v is not None else None) for k, v in dev.items()}
+        ref_o, ref_lse = oracle_ref(one, inp, rows=rows)
+        compare(one, o[:, h:h + 1].cpu(), lse[:, h:h + 1].cpu(), ref_o, ref_lse, rows=rows,
+                label=f"{wl.name}/head{h}")
