@@ -422,6 +422,36 @@ DEV PFrag softmax_p(WaveAcc& acc, const f32x16& s, float c2) {
   return pf;
 }
 
+// A band block's only global column (one global token for its batch item):
+// the key enters the online-softmax state before the band, from registers.
+// Each lane holds half of q and of k (d = 16s + 8g + e), so the score is the
+// sum over the row's two lanes; against the reference m = that score its
+// weight is exp2(0) = 1, so O starts as the key's V row (each lane its own
+// d columns) and l as 1, counted on the row's first lane.
+DEV void global_column_init(WaveAcc& acc, const QFrag<__bf16>& qf, const QFrag<__bf16>& kf,
+                            const bf16x4 (&vr)[2][4], bool allowed, float c2, int g) {
+  float part = 0.f;
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      part = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{qf.v[st][e], qf.v[st][e + 1]},
+                                              bf16x2{kf.v[st][e], kf.v[st][e + 1]}, part, false);
+  const float sc = pair_sum(part);
+  if (allowed) {
+    acc.m = sc;
+    acc.thr = sc + RESCALE_LOG2 / c2;
+    acc.moff = -sc * c2;
+    acc.l = g == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc.o[dh][4 * a + e] = (float)vr[dh][a][e];
+  }
+}
+
 DEV void pv_from(WaveAcc& acc, const VFrag& v, const PFrag& pf) {
 #pragma unroll
   for (int sp = 0; sp < 2; ++sp)
@@ -802,9 +832,12 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
   const int ngb = part == 0 ? gs.n : 0;  // the global columns go with the first key part
   int gq[4] = {0, 0, 0, 0};
   int gm = 0;
-  if (BF16 && ngb > 0) {
+  int gpos1 = 0;  // the global column when it is the only one (bf16)
+  if (BF16 && ngb > 1) {
     gather_rows(gq, gix, 0, ngb, wave, lane);
     gm = gix[min(lane, ngb - 1)];
+  } else if (BF16 && ngb == 1) {
+    gpos1 = gix[0];
   }
   const int bh = td.bh, r = td.r, q0 = td.q0, nr = td.nr;
   if (q0 >= nr) return;  // an empty residue block (uniform decode only)
@@ -840,11 +873,37 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
   acc_init(acc);
 
   if constexpr (BF16) {
+   if (ngb <= 1) {
+    // Band tiles 0 and 1, Q and (one global token) the key's K and V rows in
+    // one round trip; the global column is folded in from registers.
+    QFrag<T> kgf;
+    bf16x4 vgr[2][4];
+    if (c.nband > 0) ring_start<T>(c);
+    load_q(qf, qrow, g);
+    if (ngb == 1) {
+      const T* krow = reinterpret_cast<const T*>(kb + (long)gpos1 * ROWB);
+      const T* vrow = reinterpret_cast<const T*>(vb + (long)gpos1 * ROWB);
+      load_q(kgf, krow, g);
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) vgr[dh][a] = *reinterpret_cast<const bf16x4*>(vrow + 32 * dh + 8 * a + 4 * g);
+    }
+    wait_vmcnt<0>();
+    if (ngb == 1 && wave_live) {
+      // the key counts for this row if it is left of the row when causal and
+      // not already in the row's band
+      const int dr = gpos1 - r;
+      const bool same = dr >= 0 && dr % dil == 0;
+      const bool inband = same && dr / dil >= qi - half && dr / dil <= qi + right;
+      global_column_init(acc, qf, kgf, vgr, gpos1 <= lim && !inband, c.c2, g);
+    }
+   } else {
     // One round trip for everything the block starts with: the first
     // global-column tile into stage 2, band tiles 0 and 1 into stages 0 and
     // 1, and Q. (The gather goes first: the compiler waits for the indices
     // it needs with a count that only knows its own loads.)
-    if (ngb > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
+    dma_gather(c.a2, kb, vb, gq, wave, lane);
     if (c.nband > 0) ring_start<T>(c);
     load_q(qf, qrow, g);
     if (ngb > 0) {
@@ -864,9 +923,8 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
       }
       // the first ring step's barrier orders these reads of stage 2 before
       // the load of band tile 2 into it
-    } else {
-      wait_vmcnt<0>();
     }
+   }
   } else {
     // fp32: two ring stages; the global columns go through stage 0 first
     load_q(qf, qrow, g);
