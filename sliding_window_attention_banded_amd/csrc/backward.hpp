@@ -261,9 +261,12 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   const int ngb = gs.n;
   int gq[4] = {0, 0, 0, 0};
   int gm = 0;
-  if (ngb > 0) {
+  int gpos1 = 0;  // the global column when it is the only one
+  if (ngb > 1) {
     gather_rows(gq, gix, 0, ngb, wave, lane);
     gm = gix[min(lane, ngb - 1)];
+  } else if (ngb == 1) {
+    gpos1 = gix[0];
   }
   const int bh = td.bh, r = td.r, q0 = td.q0, nr = td.nr;
   if (q0 >= nr) return;
@@ -290,13 +293,51 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   DqWave w;
   acc2_zero(w.dq);
   const long roff = base + (long)pos_q * ROWB;
-  if (ngb > 0) dma_gather(c.a2, kb, vb, gq, wave, lane);
+  if (ngb > 1) dma_gather(c.a2, kb, vb, gq, wave, lane);
   ring_start<__bf16>(c);
   load_q(w.qf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.q) + roff), g);
   load_q(w.dof, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.dout) + roff), g);
   w.lse2 = p.lse2[(long)bh * p.n + pos_q];
   w.dd = p.dd[(long)bh * p.n + pos_q];
-  if (ngb > 0) {
+  if (ngb == 1) {
+    // One global column: its term from registers, as the forward folds it
+    // in. Score and dP are dot products over the row's two lanes; the dS
+    // weight is rounded to bf16 like the units' B operand.
+    QFrag<__bf16> kgf, vgf;
+    bf16x4 kacc[2][4];
+    const __bf16* krow = reinterpret_cast<const __bf16*>(kb + (long)gpos1 * ROWB);
+    load_q(kgf, krow, g);
+    load_q(vgf, reinterpret_cast<const __bf16*>(vb + (long)gpos1 * ROWB), g);
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) kacc[dh][a] = *reinterpret_cast<const bf16x4*>(krow + 32 * dh + 8 * a + 4 * g);
+    wait_vmcnt<0>();
+    if (wave_live) {
+      float sp = 0.f, dpp = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          sp = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w.qf.v[st][e], w.qf.v[st][e + 1]},
+                                               bf16x2{kgf.v[st][e], kgf.v[st][e + 1]}, sp, false);
+          dpp = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w.dof.v[st][e], w.dof.v[st][e + 1]},
+                                                bf16x2{vgf.v[st][e], vgf.v[st][e + 1]}, dpp, false);
+        }
+      const float sc = pair_sum(sp), dp = pair_sum(dpp);
+      const int dr = gpos1 - r;
+      const bool same = dr >= 0 && dr % dil == 0;
+      const bool inband = same && dr / dil >= qi - half && dr / dil <= qi + right;
+      const float pj = gpos1 <= lim && !inband ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc, p.c2, -w.lse2)) : 0.f;
+      const float ds = (float)(__bf16)(pj * (dp - w.dd));
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w.dq.a[dh][4 * a + e] = __builtin_fmaf(ds, (float)kacc[dh][a][e], w.dq.a[dh][4 * a + e]);
+    }
+  } else if (ngb > 1) {
     if (tid < KT) gmeta_write(gmeta, gm, tid < ngb, r, dil, tid);
     wait_vmcnt<0>();
     __syncthreads();
