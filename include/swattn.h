@@ -107,9 +107,10 @@ int swattn_create(const swattn_params* p, swattn_plan** out);
  *   lse         device fp32 [B, H, n] or NULL to skip.
  * All device pointers must be 16-byte aligned (else ALIGNMENT) and stay
  * valid until the stream reaches the enqueued work. The caller owns every
- * buffer; forward allocates nothing. Errors: INVALID_ARG (null plan or
- * tensor, NULL-ness of qg/kg/vg not matching n_global, o overlapping an
- * input), ALIGNMENT, HIP (launch failure; see swattn_last_error()).
+ * buffer; forward allocates nothing. The current HIP device must be the
+ * plan's. Errors: INVALID_ARG (null plan or tensor, NULL-ness of qg/kg/vg
+ * not matching n_global, o overlapping an input, another current device),
+ * ALIGNMENT, HIP (launch failure; see swattn_last_error()).
  */
 int swattn_forward(swattn_plan* plan, const void* q, const void* k,
                    const void* v, const void* qg, const void* kg,
@@ -132,8 +133,8 @@ int swattn_forward(swattn_plan* plan, const void* q, const void* k,
  *                     when n_global == 0.
  * Gradients must not overlap each other or any input. The plan's workspace
  * holds per-row statistics, so a plan runs one backward (or forward) at a
- * time. bf16 plans only. Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (fp32
- * plan), HIP.
+ * time. bf16 plans only; the current HIP device must be the plan's.
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (fp32 plan), HIP.
  */
 int swattn_backward(swattn_plan* plan, const void* q, const void* k, const void* v,
                     const void* qg, const void* kg, const void* vg, const void* o,

@@ -435,12 +435,25 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
 
 }  // namespace
 
+namespace {
+// The plan's memory lives on the device it was created on; kernels go to the
+// current device.
+int check_device(const swattn_plan* pl) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != pl->device) return fail(SWATTN_ERR_INVALID_ARG, "the current device is not the plan's device");
+  return SWATTN_OK;
+}
+}  // namespace
+
 extern "C" int swattn_forward(swattn_plan* pl, const void* q, const void* k, const void* v,
                               const void* qg, const void* kg, const void* vg, void* o,
                               float* lse, void* stream) {
   g_last_error.clear();
   if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
   if (!q || !k || !v || !o) return fail(SWATTN_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+  if (const int rc = check_device(pl)) return rc;
   const bool want_g = pl->ng > 0;
   if ((qg != nullptr) != want_g || (kg != nullptr) != want_g || (vg != nullptr) != want_g)
     return fail(SWATTN_ERR_INVALID_ARG, "qg, kg, vg must be non-NULL exactly when n_global > 0");
@@ -472,6 +485,7 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   if (pl->dtype != SWATTN_BF16) return fail(SWATTN_ERR_UNSUPPORTED, "the backward pass is bf16 only");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(SWATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
+  if (const int rc = check_device(pl)) return rc;
   const bool want_g = pl->ng > 0;
   const void* gs[] = {qg, kg, vg, dqg, dkg, dvg};
   for (const void* x : gs)
