@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     # no NaN canonicalisation in max/min (a NaN input gives a NaN output
     # either way; infinities are still honoured: masking relies on -inf)
     "-fno-honor-nans",
+    # kernels whose leading arguments are scalars get them in SGPRs at wave
+    # start (kernels that start with a struct argument preload nothing)
+    "-mllvm", "-amdgpu-kernarg-preload-count=4",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -1131,24 +1131,27 @@ DEV void lse_fold(float& M, float& L, float& A, float m, float l, float a, float
   M = mn;
 }
 
+// The partials' pointers and counts come first among the arguments so that
+// they can be preloaded into SGPRs (the build's kernarg-preload count): the
+// partial loads then go out as the waves start, together with the global
+// token's position, instead of after the argument fetch and the set lookup.
 template <class T>
-__global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
+__global__ __launch_bounds__(256) void global_rows_merge(const float* part_ml, const float* part_o,
+                                                         int ng, int nsplit, GlobalParams p) {
   __shared__ float sm[4][HD], sl[4][HD], sa[4][HD];
-  const int gi = blockIdx.x % p.ng, bh = blockIdx.x / p.ng, tid = threadIdx.x;
-  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
-  if (gi >= gs.n) return;
+  const int gi = blockIdx.x % ng, bh = blockIdx.x / ng, tid = threadIdx.x;
   const int d = tid & 63, grp = tid >> 6;
-  const int pos = gs.idx[gi];  // loaded with the partials, not after them
-  const long slot0 = ((long)bh * p.ng + gi) * p.nsplit;
-  const float* ml = p.part_ml + slot0 * 2;
-  const float* po = p.part_o + slot0 * HD + d;
+  // in bounds for every (bh, gi < ng); used only when gi is a row of the item
+  const long slot0 = ((long)bh * ng + gi) * nsplit;
+  const float* ml = part_ml + slot0 * 2;
+  const float* po = part_o + slot0 * HD + d;
   float M = -__builtin_inff(), L = 0.f, A = 0.f;
-  for (int b0 = grp; b0 < p.nsplit; b0 += 32) {
+  for (int b0 = grp; b0 < nsplit; b0 += 32) {
     float m[8], l[8], o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int sidx = b0 + 4 * i;
-      const bool ok = sidx < p.nsplit;
+      const bool ok = sidx < nsplit;
       m[i] = ok ? ml[2 * sidx] : -__builtin_inff();
       l[i] = ok ? ml[2 * sidx + 1] : 0.f;
       o[i] = ok ? po[(long)sidx * HD] : 0.f;
@@ -1156,6 +1159,9 @@ __global__ __launch_bounds__(256) void global_rows_merge(GlobalParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) lse_fold(M, L, A, m[i], l[i], o[i], p.c2);
   }
+  const GSet gs = batch_gset(p.gidx, p.goff, ng, bh / p.H);
+  if (gi >= gs.n) return;  // workgroup-uniform
+  const int pos = gs.idx[gi];
   sm[grp][d] = M;
   sl[grp][d] = L;
   sa[grp][d] = A;

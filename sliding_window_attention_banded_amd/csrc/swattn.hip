@@ -424,9 +424,11 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
     const dim3 mgrid(pl->ng * pl->B * pl->H);
     hipEvent_t start = pl->parts > 1 ? nullptr : (timed ? ev[2] : nullptr);
     if (timed)
-      hipExtLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, start, ev[3], 0, gp);
+      hipExtLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, start, ev[3], 0,
+                            (const float*)gp.part_ml, (const float*)gp.part_o, gp.ng, gp.nsplit, gp);
     else
-      hipLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, gp);
+      hipLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, (const float*)gp.part_ml,
+                         (const float*)gp.part_o, gp.ng, gp.nsplit, gp);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch global_rows_merge");
   }
