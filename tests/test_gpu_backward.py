@@ -58,6 +58,11 @@ SMALL = [
     W("b_g_all", 1, 2, 130, (8, 4), (1, 2), False, tuple(range(130))),
     W("b_per_item", 3, 2, 500, (64, 16), (1, 3), False, ((0, 5, 499), (), tuple(range(100, 190)))),
     W("b_per_item_causal", 2, 3, 400, (32, 256, 2), (1, 4, 1), True, ((7,), (0, 250, 399))),
+    # one global token per item (its column folded in from registers): in
+    # the middle (inside some rows' bands), dilated heads, causal, per item
+    W("b_g1_mid_dil", 2, 3, 777, (64, 128, 30), (1, 2, 3), False, (401,)),
+    W("b_g1_causal_dil", 1, 4, 500, (32, 256, 2, 1024), (1, 4, 1, 2), True, (250,)),
+    W("b_g1_per_item", 3, 2, 500, (64, 16), (1, 3), False, ((5,), (), (499,))),
 ]
 
 GRADS = ("dq", "dk", "dv", "dqg", "dkg", "dvg")
