@@ -64,7 +64,22 @@ def _draw(i):
     return Workload(f"rand{i}", B, H, n, 64, win, dil, causal, G, "bf16"), kind
 
 
-CONFIGS = [_draw(i) for i in range(N_CONFIGS)]
+def _draw_one_global(i):
+    """At most one global token per batch item (the configuration in which
+    the band blocks fold the global column in from registers): a shared
+    token, or one per item with some items having none."""
+    wl, kind = _draw(2000 + i)
+    rng = np.random.default_rng(3000 + i)
+    n, B = wl.n, wl.batch
+    if i % 2 == 0:
+        G = (int(rng.integers(0, n)),)
+    else:
+        G = tuple(((int(rng.integers(0, n)),) if rng.random() < 0.7 else ()) for _ in range(B))
+    return Workload(f"rand1g{i}", B, wl.heads, n, 64, wl.window, wl.dilation, i % 4 < 2, G,
+                    "bf16"), kind
+
+
+CONFIGS = [_draw(i) for i in range(N_CONFIGS)] + [_draw_one_global(i) for i in range(16)]
 
 
 @pytest.mark.parametrize("wl,kind", CONFIGS, ids=[c[0].name for c in CONFIGS])
