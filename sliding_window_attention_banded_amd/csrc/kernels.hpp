@@ -90,6 +90,7 @@ struct BandParams {
   // part[(b*h*n + position) * parts + k][68] for band_merge (parts = 1: none)
   int parts;
   float* part;
+  int fair;     // progress-based wave priorities (no global-row blocks in the launch)
   int H;
   int n;
   int causal;
@@ -295,9 +296,10 @@ template <class T> DEV constexpr int key_of_reg(int j, int g) {
 // the stale m stay below 2^RESCALE_LOG2, which fp32 accumulators and the bf16
 // P operand hold without loss of relative precision. O = acc / l and
 // LSE = m*scale + ln l are the same quantities as with an exact running max.
-// In bf16 the row sum l is the sum of the bf16-rounded weights, so O is an
-// exact convex combination of V rows up to fp32 rounding, and LSE carries at
-// most the 2^-8 relative rounding of a weight.
+// In bf16 the P V product takes the weights rounded to bf16 while the row
+// sum l adds the unrounded fp32 weights, so LSE carries fp32 rounding only
+// and O the bf16 rounding of each weight (relative 2^-9), which averages
+// out over the row.
 constexpr float RESCALE_LOG2 = 8.0f;
 
 // fp32 path: online softmax of one 32-key unit and O += P V.
@@ -406,7 +408,6 @@ DEV PFrag softmax_p(WaveAcc& acc, const f32x16& s, float c2) {
     acc.thr = acc.m + RESCALE_LOG2 / c2;
     acc.moff = acc.m == -__builtin_inff() ? 0.f : -acc.m * c2;
   }
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   PFrag pf;
   float l = acc.l;
 #pragma unroll
@@ -414,7 +415,7 @@ DEV PFrag softmax_p(WaveAcc& acc, const f32x16& s, float c2) {
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, acc.moff));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c2, acc.moff));
     const bf16x2 t = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-    l = __builtin_amdgcn_fdot2_f32_bf16(t, one, l, false);
+    l += p0 + p1;
     pf.b[j >> 3][j & 7] = t[0];
     pf.b[j >> 3][(j & 7) + 1] = t[1];
   }
@@ -619,7 +620,15 @@ struct RingCtx {
   bool live;            // this wave has query rows to compute
   float c2;
   LdsLanes ll;          // lane offsets of the bf16 fragment reads
+  int rot;              // the ring visits tiles rot, rot+1, .., nband-1, 0, .., rot-1
+  bool fair;            // set wave priorities by the tiles left (band blocks)
 };
+
+// Tile index (0 .. nband-1) of ring step s.
+DEV int ring_tile(const RingCtx& c, int s) {
+  const int t = s + c.rot;
+  return t < c.nband ? t : t - c.nband;
+}
 
 // Which 32-key units a band wave computes and how they are masked: row qi
 // sees keys qi - half .. qi + right of its residue class, clipped to nr.
@@ -663,13 +672,23 @@ DEV void ring_step(int tb, WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, c
   const char* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
   constexpr int SN = (S + NS - 1) % NS;
   const unsigned nxt = SN == 0 ? c.a0 : (SN == 1 ? c.a1 : c.a2);
+  if (c.fair) {
+    // the workgroups sharing a CU otherwise run oldest-first, which leaves
+    // the last one alone on the CU at the end; waves with more tiles left
+    // issue first, so the co-resident workgroups finish together
+    const int rem = c.nband - tb;
+    if (rem >= 9) __builtin_amdgcn_s_setprio(3);
+    else if (rem >= 6) __builtin_amdgcn_s_setprio(2);
+    else if (rem >= 3) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
   wait_vmcnt<NS == 3 ? Dma<T>::PER_WAVE : 0>();
   wg_barrier();  // tile tb has landed for every wave; tile tb-1 is consumed
-  const int kn = c.kbeg + min(tb + NS - 1, c.nband - 1) * KT;
+  const int kn = c.kbeg + ring_tile(c, min(tb + NS - 1, c.nband - 1)) * KT;
   if (kn + KT <= c.kend) dma_tile_fast<T>(nxt, dl, c.kb, c.vb, kn, c.r, c.dil, c.wave);
   else dma_tile<T>(nxt, c.kb, c.vb, kn, c.kend, c.r, c.dil, c.wave, c.lane);
   if (!c.live) return;
-  const int k0 = c.kbeg + tb * KT;
+  const int k0 = c.kbeg + ring_tile(c, tb) * KT;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const int ku = k0 + 32 * kh;
@@ -697,9 +716,10 @@ template <> struct RingCfg<float> { static constexpr int NS = 2; };
 // Start the ring: DMA of tile 0 (and 1 with three stages).
 template <class T>
 DEV void ring_start(const RingCtx& c) {
-  dma_tile<T>(c.a0, c.kb, c.vb, c.kbeg, c.kend, c.r, c.dil, c.wave, c.lane);
+  dma_tile<T>(c.a0, c.kb, c.vb, c.kbeg + ring_tile(c, 0) * KT, c.kend, c.r, c.dil, c.wave, c.lane);
   if (RingCfg<T>::NS == 3)
-    dma_tile<T>(c.a1, c.kb, c.vb, c.kbeg + min(1, c.nband - 1) * KT, c.kend, c.r, c.dil, c.wave, c.lane);
+    dma_tile<T>(c.a1, c.kb, c.vb, c.kbeg + ring_tile(c, min(1, c.nband - 1)) * KT, c.kend, c.r, c.dil,
+                c.wave, c.lane);
 }
 
 // Run every tile of the ring (ring_start has been issued and, with it, any
@@ -812,6 +832,22 @@ DEV void glob_cols_tile(WaveAcc& acc, const QFrag<T>& qf, const RingCtx& c, cons
   }
 }
 
+// First ring step of a band block. Consecutive 128-row blocks of a residue
+// class share most of their key tiles; blocks are taken in groups of
+// (half + right + BM) / BM, about the number of blocks whose windows meet one
+// key, and every block of a group starts at the tile that holds the middle of
+// the group's middle block (clipped to its own band), then wraps around its
+// band. At the start of the kernel, when every block fetches at once, a
+// group then asks memory for one tile instead of one per block; the order of
+// the tiles does not change the result.
+DEV int band_rotation(int q0, int kbeg, int nband, int half, int right) {
+  const int gs = max(1, (half + right + BM) / BM);
+  const int qb = q0 / BM;
+  const int anchor = (qb / gs * gs + gs / 2) * BM + BM / 2;
+  const int t = anchor >= kbeg ? (anchor - kbeg) / KT : 0;
+  return min(t, nband - 1);
+}
+
 template <class T>
 DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st1, char* st2,
                     int (*gmeta)[KT]) {
@@ -866,6 +902,8 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
             (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg + t0 * KT, kend, t1 - t0, r, dil,
             wave, lane, g, wave_live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
+  if (p.parts == 1) c.rot = band_rotation(q0, kbeg, c.nband, half, right);
+  c.fair = p.fair != 0;
   const BandPol pol{qi, qw0, half, right, nr, wk_lo, wk_hi};
   const T* qrow = reinterpret_cast<const T*>(reinterpret_cast<const char*>(p.q) + base + (long)pos_q * ROWB);
   QFrag<T> qf;

@@ -382,6 +382,7 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
   bp.uni_nqb = pl->uni_nqb;
   bp.parts = pl->parts; bp.part = pl->band_part;
+  bp.fair = pl->ng == 0 ? 1 : 0;
   bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   GlobalParams gp;
