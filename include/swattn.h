@@ -117,6 +117,31 @@ int swattn_forward(swattn_plan* plan, const void* q, const void* k,
                    const void* vg, void* o, float* lse, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward pass as swattn_create + swattn_forward + swattn_destroy, in one
+ * call that allocates nothing. The parameters are those of swattn_create and
+ * are validated the same way; the tensors are those of swattn_forward, with
+ * the same rules. The schedule tables and the partial results exchanged
+ * between the kernels live in a 32 MiB array in device memory that the
+ * library reserves statically (each GPU it runs on holds one copy until the
+ * process ends) instead of in a plan; the tables reach it through the
+ * arguments of small copy kernels enqueued on `stream`, so no host buffer
+ * must outlive the call. Nothing in the array has to start at zero: every
+ * entry a kernel reads was written earlier in the same call. Every call on
+ * one GPU uses that GPU's array, so two calls whose work overlaps in time
+ * on one GPU (different streams, or host threads) race and may return wrong
+ * results: serialise them. Enqueues work and returns without waiting.
+ * Errors: as swattn_create and swattn_forward; UNSUPPORTED also when the
+ * problem needs more than 32 MiB of that array (its global-row partials,
+ * B*H*|G|*ceil(n/256)*264 bytes, plus its key-split partials, B*H*n*parts*
+ * 272 bytes, plus the tables), or the device index is above 63.
+ */
+int swattn_forward_noalloc(const swattn_params* p, const void* q, const void* k,
+                           const void* v, const void* qg, const void* kg,
+                           const void* vg, void* o, float* lse, void* stream);
+
+/*
  * Enqueue the backward pass of one forward on `stream` and return without
  * waiting: the gradients of Q, K, V (and of Qg, Kg, Vg) for a cotangent dout
  * of O. With P_ij = exp(s q_i.k_j - LSE_i) on the key set A(i) of the

@@ -6,7 +6,7 @@ this package does not load the library; creating a ``Plan`` does, and fails
 loudly when the library is missing.
 """
 
-__all__ = ["Plan", "SwattnError", "project", "library_path"]
+__all__ = ["Plan", "SwattnError", "project", "forward_noalloc", "library_path"]
 
 
 def __getattr__(name):

@@ -13,12 +13,14 @@ import os
 
 import torch
 
-__all__ = ["Plan", "SwattnError", "project", "library_path", "load_library", "EXPORTS"]
+__all__ = ["Plan", "SwattnError", "project", "forward_noalloc", "library_path", "load_library",
+           "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIGNMENT = range(5)
 BF16, FP32 = 0, 1
-EXPORTS = ("swattn_create", "swattn_forward", "swattn_backward", "swattn_project", "swattn_destroy",
+EXPORTS = ("swattn_create", "swattn_forward", "swattn_forward_noalloc", "swattn_backward",
+           "swattn_project", "swattn_destroy",
            "swattn_set_timing", "swattn_kernel_times",
            "swattn_status_string", "swattn_last_error")
 
@@ -63,6 +65,8 @@ def load_library():
     lib.swattn_create.restype = ctypes.c_int
     lib.swattn_forward.argtypes = [vp] * 8 + [vp, vp]
     lib.swattn_forward.restype = ctypes.c_int
+    lib.swattn_forward_noalloc.argtypes = [ctypes.POINTER(_Params)] + [vp] * 9
+    lib.swattn_forward_noalloc.restype = ctypes.c_int
     lib.swattn_backward.argtypes = [vp] * 17
     lib.swattn_backward.restype = ctypes.c_int
     lib.swattn_project.argtypes = [vp] * 4 + [ctypes.c_int] * 6 + [vp]
@@ -92,20 +96,12 @@ def _check(lib, status, what):
 _DT = {torch.bfloat16: BF16, torch.float32: FP32}
 
 
-class Plan:
-    """A configured banded-attention forward: ``Plan(...).forward(q, k, v)``.
+class _ParamSet:
+    """swattn_params for one configuration, with the host arrays it points
+    to kept alive as long as this object."""
 
-    ``window`` and ``dilation`` are per head (a scalar is broadcast);
-    ``global_idx`` lists the global-token positions shared by all batch items
-    and heads, or gives one such list per batch item. Tensors are
-    [B, H, n, 64] contiguous CUDA tensors in ``dtype``. ``key_split``: 0 lets
-    the library share the band keys over several workgroups when the problem
-    is too small to fill the GPU; 1 never does; k >= 2 always uses k parts.
-    """
-
-    def __init__(self, batch, heads, n, d=64, window=512, dilation=1,
-                 causal=False, global_idx=(), dtype=torch.bfloat16, key_split=0):
-        self._lib = load_library()
+    def __init__(self, batch, heads, n, d, window, dilation, causal, global_idx, dtype,
+                 key_split):
         if dtype not in _DT:
             raise SwattnError(ERR_UNSUPPORTED, f"dtype {dtype} not supported")
         win = [int(window)] * heads if isinstance(window, int) else [int(x) for x in window]
@@ -128,18 +124,49 @@ class Plan:
             offs = None
             self.global_idx = tuple(gl)
         self.has_globals = bool(gl)
+        self.window, self.dilation = tuple(win), tuple(dil)
+        self._W = (ctypes.c_int32 * heads)(*win)
+        self._D = (ctypes.c_int32 * heads)(*dil)
+        self._G = (ctypes.c_int32 * max(1, len(gl)))(*gl) if gl else None
+        self._O = (ctypes.c_int32 * len(offs))(*offs) if offs else None
+        self.params = _Params(batch, heads, n, d, self._W, self._D, int(bool(causal)),
+                              ctypes.cast(self._G, ctypes.POINTER(ctypes.c_int32)) if self._G else None,
+                              len(gl), _DT[dtype],
+                              ctypes.cast(self._O, ctypes.POINTER(ctypes.c_int32)) if self._O else None,
+                              int(key_split))
+
+
+def _check_lse(lse, shape, device):
+    if lse is None:
+        return None
+    if not lse.is_cuda or lse.device != device:
+        raise SwattnError(ERR_INVALID_ARG, "lse must be a device tensor on the inputs' device")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != shape:
+        raise SwattnError(ERR_INVALID_ARG, "lse must be contiguous fp32 [B, H, n]")
+    return lse.data_ptr()
+
+
+class Plan:
+    """A configured banded-attention forward: ``Plan(...).forward(q, k, v)``.
+
+    ``window`` and ``dilation`` are per head (a scalar is broadcast);
+    ``global_idx`` lists the global-token positions shared by all batch items
+    and heads, or gives one such list per batch item. Tensors are
+    [B, H, n, 64] contiguous CUDA tensors in ``dtype``. ``key_split``: 0 lets
+    the library share the band keys over several workgroups when the problem
+    is too small to fill the GPU; 1 never does; k >= 2 always uses k parts.
+    """
+
+    def __init__(self, batch, heads, n, d=64, window=512, dilation=1,
+                 causal=False, global_idx=(), dtype=torch.bfloat16, key_split=0):
+        self._lib = load_library()
+        ps = _ParamSet(batch, heads, n, d, window, dilation, causal, global_idx, dtype, key_split)
+        self.global_idx = ps.global_idx
+        self.has_globals = ps.has_globals
         self.batch, self.heads, self.n, self.d = batch, heads, n, d
-        self.window, self.dilation, self.causal = tuple(win), tuple(dil), bool(causal)
+        self.window, self.dilation, self.causal = ps.window, ps.dilation, bool(causal)
         self.dtype = dtype
-        W = (ctypes.c_int32 * heads)(*win)
-        D = (ctypes.c_int32 * heads)(*dil)
-        G = (ctypes.c_int32 * max(1, len(gl)))(*gl) if gl else None
-        O = (ctypes.c_int32 * len(offs))(*offs) if offs else None
-        p = _Params(batch, heads, n, d, W, D, int(bool(causal)),
-                    ctypes.cast(G, ctypes.POINTER(ctypes.c_int32)) if G else None,
-                    len(gl), _DT[dtype],
-                    ctypes.cast(O, ctypes.POINTER(ctypes.c_int32)) if O else None,
-                    int(key_split))
+        p = ps.params
         h = ctypes.c_void_p()
         _check(self._lib, self._lib.swattn_create(ctypes.byref(p), ctypes.byref(h)),
                "swattn_create")
@@ -268,3 +295,40 @@ def project(x, weight, bias=None, heads=None, out=None, stream=None):
                                    ctypes.c_void_p(st.cuda_stream)),
            "swattn_project")
     return out
+
+
+def forward_noalloc(q, k, v, qg=None, kg=None, vg=None, window=512, dilation=1, causal=False,
+                    global_idx=(), key_split=0, out=None, lse=None, want_lse=False, stream=None):
+    """One forward through swattn_forward_noalloc: no plan, no device
+    allocation inside the library (its tables and partial results live in a
+    statically reserved device array shared by every call on the GPU, so
+    calls must not overlap). Same arguments and result as
+    ``Plan(...).forward``; the shape and dtype come from ``q``."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise SwattnError(ERR_INVALID_ARG, "q must be [B, H, n, d]")
+    batch, heads, n, d = (int(x) for x in q.shape)
+    ps = _ParamSet(batch, heads, n, d, window, dilation, causal, global_idx, q.dtype, key_split)
+    shape = (batch, heads, n, d)
+
+    def ptr(t, name):
+        if t is None:
+            return None
+        if not t.is_cuda or t.device != q.device:
+            raise SwattnError(ERR_INVALID_ARG, f"{name} must be a device tensor on q's device")
+        if t.dtype != q.dtype or tuple(t.shape) != shape or not t.is_contiguous():
+            raise SwattnError(ERR_INVALID_ARG, f"{name} must be contiguous {q.dtype} of shape {shape}")
+        return t.data_ptr()
+
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((batch, heads, n), dtype=torch.float32, device=q.device)
+    lp = _check_lse(lse, (batch, heads, n), q.device)
+    ptrs = [ptr(q, "q"), ptr(k, "k"), ptr(v, "v"), ptr(qg, "qg"), ptr(kg, "kg"), ptr(vg, "vg"),
+            ptr(out, "out"), lp]
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _check(lib, lib.swattn_forward_noalloc(ctypes.byref(ps.params), *ptrs,
+                                           ctypes.c_void_p(st.cuda_stream)),
+           "swattn_forward_noalloc")
+    return out, lse

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -86,9 +87,26 @@ extern "C" const char* swattn_status_string(int status) {
 
 extern "C" const char* swattn_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
-  g_last_error.clear();
-  if (!p || !out) return fail(SWATTN_ERR_INVALID_ARG, "params and out must not be NULL");
+namespace {
+
+// Everything the forward needs that follows from the parameters alone
+// (host side, no device memory): validated geometry, the sorted global
+// sets, the band tile schedule, the key split and the global-row chunks.
+struct Schedule {
+  int ng_max = 0;
+  bool per_item = false;
+  std::vector<int> G, goff;
+  std::vector<TileRec> tiles;  // empty when every head has the same geometry
+  std::vector<int> half, dil;
+  long nband_blocks = 0;
+  int parts = 1;
+  int cus = 256;
+  int nsplit = 0, ksplit = 0, nqb = 0, ngroup = 0;
+  long nglob_blocks = 0;
+};
+
+int make_schedule(const swattn_params* p, Schedule* sc) {
+  if (!p) return fail(SWATTN_ERR_INVALID_ARG, "params must not be NULL");
   if (p->batch < 1 || p->heads < 1) return fail(SWATTN_ERR_INVALID_ARG, "batch and heads must be >= 1");
   if (p->n < 1 || p->n > (1 << 24)) return fail(SWATTN_ERR_INVALID_ARG, "n must be in [1, 2^24]");
   if (p->causal != 0 && p->causal != 1) return fail(SWATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -199,12 +217,49 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
 
   // the backward launch holds two blocks per band tile
   if (2 * nband_blocks > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many tiles");
+  sc->ng_max = ng_max;
+  sc->per_item = per_item && ng_max > 0;
+  sc->G = std::move(G);
+  sc->goff = std::move(goff);
+  sc->tiles = std::move(tiles);
+  sc->half = std::move(half);
+  sc->dil = std::move(dil);
+  sc->nband_blocks = nband_blocks;
+  sc->parts = parts;
+  sc->cus = cus;
+  sc->nqb = (ng_max + 31) / 32;
+  sc->ngroup = (sc->nqb + BAND_WAVES - 1) / BAND_WAVES;
+  if (ng_max > 0) {
+    choose_split(p->n, &sc->nsplit, &sc->ksplit);
+    sc->nglob_blocks = (long)sc->nsplit * sc->ngroup * bh;
+    if (sc->nglob_blocks + nband_blocks * parts > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+  }
+  return SWATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
+  g_last_error.clear();
+  if (!p || !out) return fail(SWATTN_ERR_INVALID_ARG, "params and out must not be NULL");
+  Schedule sc;
+  if (const int rc = make_schedule(p, &sc)) return rc;
+  const long bh = (long)p->batch * p->heads;
+  const int ng_max = sc.ng_max;
+  const long nband_blocks = sc.nband_blocks;
+  const int parts = sc.parts;
+  const std::vector<int>& G = sc.G;
+  const std::vector<int>& goff = sc.goff;
+  const std::vector<TileRec>& tiles = sc.tiles;
+  const std::vector<int>& half = sc.half;
+  const std::vector<int>& dil = sc.dil;
+  const size_t split_bytes = parts > 1 ? (size_t)bh * p->n * parts * PART_STRIDE * sizeof(float) : 0;
 
   swattn_plan* pl = new (std::nothrow) swattn_plan();
   if (!pl) return fail(SWATTN_ERR_HIP, "host allocation failed");
   pl->B = p->batch; pl->H = p->heads; pl->n = p->n; pl->d = p->d;
   pl->causal = p->causal; pl->ng = ng_max; pl->dtype = p->dtype;
-  pl->per_item = per_item && ng_max > 0;
+  pl->per_item = sc.per_item;
   pl->nband_blocks = (int)nband_blocks;
   pl->parts = parts;
   pl->band_part = nullptr;
@@ -212,19 +267,11 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->uni_right = p->causal ? 0 : half[0];
   pl->uni_dil = dil[0];
   pl->uni_nqb = ((p->n + dil[0] - 1) / dil[0] + BM - 1) / BM;
-  pl->nqb = (pl->ng + 31) / 32;
-  pl->ngroup = (pl->nqb + BAND_WAVES - 1) / BAND_WAVES;
-  pl->nsplit = pl->ksplit = 0;
-  pl->nglob_blocks = 0;
-  if (pl->ng > 0) {
-    choose_split(p->n, &pl->nsplit, &pl->ksplit);
-    const long nglob = (long)pl->nsplit * pl->ngroup * bh;
-    if (nglob + nband_blocks * parts > 0x7fffffffL) {
-      delete pl;
-      return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
-    }
-    pl->nglob_blocks = (int)nglob;
-  }
+  pl->nqb = sc.nqb;
+  pl->ngroup = sc.ngroup;
+  pl->nsplit = sc.nsplit;
+  pl->ksplit = sc.ksplit;
+  pl->nglob_blocks = (int)sc.nglob_blocks;
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
 
@@ -450,33 +497,163 @@ int check_device(const swattn_plan* pl) {
 }
 }  // namespace
 
-extern "C" int swattn_forward(swattn_plan* pl, const void* q, const void* k, const void* v,
-                              const void* qg, const void* kg, const void* vg, void* o,
-                              float* lse, void* stream) {
-  g_last_error.clear();
-  if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
+namespace {
+// The tensor arguments of a forward: NULL-ness, alignment, no overlap of an
+// output with an input.
+int check_forward_args(long B, long H, long n, int dtype, int ng, const void* q, const void* k,
+                       const void* v, const void* qg, const void* kg, const void* vg, const void* o,
+                       const float* lse) {
   if (!q || !k || !v || !o) return fail(SWATTN_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
-  if (const int rc = check_device(pl)) return rc;
-  const bool want_g = pl->ng > 0;
+  const bool want_g = ng > 0;
   if ((qg != nullptr) != want_g || (kg != nullptr) != want_g || (vg != nullptr) != want_g)
     return fail(SWATTN_ERR_INVALID_ARG, "qg, kg, vg must be non-NULL exactly when n_global > 0");
   const void* all[] = {q, k, v, qg, kg, vg, o, lse};
   for (const void* x : all)
     if (x && !aligned16(x)) return fail(SWATTN_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  const size_t es = pl->dtype == SWATTN_BF16 ? 2 : 4;
-  const size_t nbytes = (size_t)pl->B * pl->H * pl->n * HD * es;
+  const size_t es = dtype == SWATTN_BF16 ? 2 : 4;
+  const size_t nbytes = (size_t)B * H * n * HD * es;
   const void* ins[] = {q, k, v, qg, kg, vg};
   for (const void* x : ins)
     if (overlaps(o, nbytes, x, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "o overlaps an input");
   if (lse) {
-    const size_t lb = (size_t)pl->B * pl->H * pl->n * sizeof(float);
+    const size_t lb = (size_t)B * H * n * sizeof(float);
     for (const void* x : ins)
       if (overlaps(lse, lb, x, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "lse overlaps an input");
     if (overlaps(lse, lb, o, nbytes)) return fail(SWATTN_ERR_INVALID_ARG, "lse overlaps o");
   }
+  return SWATTN_OK;
+}
+}  // namespace
+
+extern "C" int swattn_forward(swattn_plan* pl, const void* q, const void* k, const void* v,
+                              const void* qg, const void* kg, const void* vg, void* o,
+                              float* lse, void* stream) {
+  g_last_error.clear();
+  if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
+  if (const int rc = check_forward_args(pl->B, pl->H, pl->n, pl->dtype, pl->ng, q, k, v, qg, kg, vg, o, lse))
+    return rc;
+  if (const int rc = check_device(pl)) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (pl->dtype == SWATTN_BF16) return launch<__bf16>(pl, q, k, v, qg, kg, vg, o, lse, st);
   return launch<float>(pl, q, k, v, qg, kg, vg, o, lse, st);
+}
+
+// ----------------------------------------------------------------------------
+// Allocation-free forward. The tables a plan would hold (tile list, global
+// sets) and the partial results its kernels exchange (global-row chunks,
+// key-split parts) live in one file-scope device array instead; its address
+// on each device is looked up once, with that device current, and used for
+// every launch there. Small host tables reach it through the arguments of a
+// copy kernel, so nothing is allocated and nothing host-side must outlive
+// the call.
+
+namespace {
+
+constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_on_current_device(unsigned char** out, int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(SWATTN_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  *dev_out = dev;
+  return SWATTN_OK;
+}
+
+constexpr int UPLOAD_CHUNK = 2048;
+struct UploadArgs {
+  unsigned char* dst;
+  int nbytes;
+  unsigned char data[UPLOAD_CHUNK];
+};
+
+__global__ __launch_bounds__(256) void upload_bytes(UploadArgs a) {
+  for (int i = threadIdx.x; i < a.nbytes; i += blockDim.x) a.dst[i] = a.data[i];
+}
+
+}  // namespace
+
+extern "C" int swattn_forward_noalloc(const swattn_params* p, const void* q, const void* k,
+                                      const void* v, const void* qg, const void* kg, const void* vg,
+                                      void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  if (!p) return fail(SWATTN_ERR_INVALID_ARG, "params must not be NULL");
+  Schedule sc;
+  if (const int rc = make_schedule(p, &sc)) return rc;
+  if (const int rc = check_forward_args(p->batch, p->heads, p->n, p->dtype, sc.ng_max, q, k, v, qg, kg, vg,
+                                        o, lse))
+    return rc;
+  unsigned char* base = nullptr;
+  int dev = -1;
+  if (const int rc = scratch_on_current_device(&base, &dev)) return rc;
+
+  // layout in the scratch array (256-byte aligned pieces)
+  const long bh = (long)p->batch * p->heads;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t o_tiles = 0;
+  const size_t o_g = o_tiles + al(sizeof(TileRec) * sc.tiles.size());
+  const size_t o_goff = o_g + al(sizeof(int) * sc.G.size());
+  const size_t o_po = o_goff + al(sizeof(int) * sc.goff.size());
+  const size_t nslot = (size_t)bh * sc.ng_max * sc.nsplit;
+  const size_t o_pml = o_po + al(sizeof(float) * HD * nslot);
+  const size_t o_part = o_pml + al(sizeof(float) * 2 * nslot);
+  const size_t split_bytes = sc.parts > 1 ? (size_t)bh * p->n * sc.parts * PART_STRIDE * sizeof(float) : 0;
+  const size_t total = o_part + al(split_bytes);
+  if (total > SCRATCH_BYTES)
+    return fail(SWATTN_ERR_UNSUPPORTED, "swattn_forward_noalloc: this problem needs " + std::to_string(total) +
+                                            " bytes of scratch, above the " + std::to_string(SCRATCH_BYTES) +
+                                            "-byte static array (use a plan)");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the host tables, laid out as in the scratch array, through copy kernels
+  std::vector<unsigned char> host(o_po, 0);
+  if (!sc.tiles.empty()) std::memcpy(host.data() + o_tiles, sc.tiles.data(), sizeof(TileRec) * sc.tiles.size());
+  if (!sc.G.empty()) std::memcpy(host.data() + o_g, sc.G.data(), sizeof(int) * sc.G.size());
+  std::memcpy(host.data() + o_goff, sc.goff.data(), sizeof(int) * sc.goff.size());
+  for (size_t off = 0; off < host.size(); off += UPLOAD_CHUNK) {
+    UploadArgs ua;
+    ua.dst = base + off;
+    ua.nbytes = (int)std::min<size_t>(UPLOAD_CHUNK, host.size() - off);
+    std::memcpy(ua.data, host.data() + off, (size_t)ua.nbytes);
+    hipLaunchKernelGGL(upload_bytes, dim3(1), dim3(256), 0, st, ua);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch upload_bytes");
+  }
+
+  // a plan on the stack whose device pointers all point into the scratch array
+  swattn_plan pl = swattn_plan();
+  pl.B = p->batch; pl.H = p->heads; pl.n = p->n; pl.d = p->d;
+  pl.causal = p->causal; pl.ng = sc.ng_max; pl.dtype = p->dtype; pl.device = dev;
+  pl.nband_blocks = (int)sc.nband_blocks;
+  pl.uni_half = sc.half[0];
+  pl.uni_right = p->causal ? 0 : sc.half[0];
+  pl.uni_dil = sc.dil[0];
+  pl.uni_nqb = ((p->n + sc.dil[0] - 1) / sc.dil[0] + BM - 1) / BM;
+  pl.nsplit = sc.nsplit; pl.ksplit = sc.ksplit; pl.nqb = sc.nqb; pl.ngroup = sc.ngroup;
+  pl.nglob_blocks = (int)sc.nglob_blocks;
+  pl.parts = sc.parts;
+  pl.per_item = sc.per_item;
+  pl.tiles = sc.tiles.empty() ? nullptr : reinterpret_cast<TileRec*>(base + o_tiles);
+  pl.gidx = reinterpret_cast<int*>(base + o_g);
+  pl.goff = sc.per_item ? reinterpret_cast<int*>(base + o_goff) : nullptr;
+  pl.part_o = reinterpret_cast<float*>(base + o_po);
+  pl.part_ml = reinterpret_cast<float*>(base + o_pml);
+  pl.band_part = sc.parts > 1 ? reinterpret_cast<float*>(base + o_part) : nullptr;
+  if (p->dtype == SWATTN_BF16) return launch<__bf16>(&pl, q, k, v, qg, kg, vg, o, lse, st);
+  return launch<float>(&pl, q, k, v, qg, kg, vg, o, lse, st);
 }
 
 extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, const void* v,
