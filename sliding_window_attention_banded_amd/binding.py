@@ -193,12 +193,10 @@ class Plan:
         if lse is None and want_lse:
             lse = torch.empty((self.batch, self.heads, self.n), dtype=torch.float32,
                               device=q.device)
-        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                                or tuple(lse.shape) != (self.batch, self.heads, self.n)):
-            raise SwattnError(ERR_INVALID_ARG, "lse must be contiguous fp32 [B, H, n]")
+        lp = _check_lse(lse, (self.batch, self.heads, self.n), q.device)
         ptrs = [self._ptr(q, "q"), self._ptr(k, "k"), self._ptr(v, "v"),
                 self._ptr(qg, "qg"), self._ptr(kg, "kg"), self._ptr(vg, "vg"),
-                self._ptr(out, "out"), lse.data_ptr() if lse is not None else None]
+                self._ptr(out, "out"), lp]
         st = stream if stream is not None else torch.cuda.current_stream(q.device)
         _check(self._lib, self._lib.swattn_forward(self._h, *ptrs, ctypes.c_void_p(st.cuda_stream)),
                "swattn_forward")
@@ -214,9 +212,9 @@ class Plan:
         ``grads`` may supply the six output tensors."""
         if self._h is None:
             raise SwattnError(ERR_INVALID_ARG, "plan is closed")
-        if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
-                or tuple(lse.shape) != (self.batch, self.heads, self.n):
+        if lse is None:
             raise SwattnError(ERR_INVALID_ARG, "lse must be contiguous fp32 [B, H, n]")
+        lp = _check_lse(lse, (self.batch, self.heads, self.n), q.device)
         has_g = self.has_globals
         if grads is None:
             grads = tuple(torch.empty_like(q) if (i < 3 or has_g) else None for i in range(6))
@@ -224,7 +222,7 @@ class Plan:
         gp = [self._ptr(t, nm) for t, nm in zip(grads, names)]
         ptrs = [self._ptr(q, "q"), self._ptr(k, "k"), self._ptr(v, "v"),
                 self._ptr(qg, "qg"), self._ptr(kg, "kg"), self._ptr(vg, "vg"),
-                self._ptr(o, "o"), lse.data_ptr(), self._ptr(dout, "dout")] + gp
+                self._ptr(o, "o"), lp, self._ptr(dout, "dout")] + gp
         st = stream if stream is not None else torch.cuda.current_stream(q.device)
         _check(self._lib, self._lib.swattn_backward(self._h, *ptrs, ctypes.c_void_p(st.cuda_stream)),
                "swattn_backward")

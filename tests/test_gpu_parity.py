@@ -114,6 +114,41 @@ def test_full_size_sampled_rows(name, kind):
     _case(wl, 0, kind, rows=_sample_rows(wl))
 
 
+@pytest.mark.parametrize("name", ["encoder_b2_h12_n4096_w512_g1", "encoder_b2_h12_n4096_w512",
+                                  "arlm_b1_h12_n8192_w512_causal_dil2", "qa_b4_h12_n4096_w512_g64"])
+@pytest.mark.parametrize("kind", ["sharp", "dedup"])
+def test_full_size_whole_tensors(name, kind):
+    """Every row of every (batch, head) of the full-size workloads, in the
+    launch configuration the benchmark times."""
+    wl = WORKLOADS[name]
+    if kind == "dedup" and not has_globals(wl):
+        pytest.skip("dedup inputs need global tokens")
+    _case(wl, 0, kind)
+
+
+@pytest.mark.parametrize("name,bh", [
+    ("arlm_b1_h8_n23040_w1024_causal_dil4", (0, 0)),   # dilation 1
+    ("arlm_b1_h8_n23040_w1024_causal_dil4", (0, 7)),   # dilation 4
+    ("led_b1_h12_n16384_w1024_g1", (0, 0)),
+    ("led_b1_h12_n16384_w1024_g1", (0, 11)),
+])
+@pytest.mark.parametrize("kind", ["sharp", "normal"])
+def test_full_size_whole_slices(name, bh, kind):
+    """Whole (batch, head) slices of the two longest workloads: every row of
+    the slice against the oracle on that slice alone."""
+    wl = WORKLOADS[name]
+    b, h = bh
+    print(f"[parity] {wl.name} slice {bh} kind={kind}", flush=True)
+    inp = make_inputs(wl, 0, kind)
+    o, lse = run_gpu(wl, inp)
+    one = wl.with_(name=f"{wl.name}[{b},{h}]", batch=1, heads=1, window=(wl.window[h],),
+                   dilation=(wl.dilation[h],),
+                   global_idx=tuple(global_union(wl)) if has_globals(wl) else ())
+    sl = {k: (v[b:b + 1, h:h + 1] if v is not None else None) for k, v in inp.items()}
+    ref_o, ref_lse = oracle_ref(one, sl)
+    compare(one, o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ref_o, ref_lse, label=one.name)
+
+
 def test_full_size_headline_all_seeds():
     wl = WORKLOADS["encoder_b2_h12_n4096_w512_g1"]
     for seed in (1, 2):
