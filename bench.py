@@ -7,7 +7,9 @@ Prints ONE JSON line. The throughput `value` is band TFLOP/s (4*d*sum of
 window keys per row, the closed form of the Longformer window), measured over
 K steps that rotate through enough input sets to exceed the 256 MB Infinity
 Cache; the warm (single input set) figure, the median of 10 samples of K
-steps, is reported beside it. The same
+steps, is reported beside it. "workloads" holds the same forward measured
+on the other workloads of the family (the encoder without global tokens,
+the AR-LM shapes, QA with 64 global tokens, the LED encoder). The same
 line carries the backward pass of the workload ("backward") and the
 projections in front of it ("projection": Q, K, V and, with global tokens,
 Qg, Kg, Vg from an input of d_model = heads*64 features), each timed the
@@ -134,6 +136,78 @@ def _cpu_banded(wl, f64, seconds):
                       f"plus the global columns (NumPy + BLAS), {dt:.1f} s"}
 
 
+# The other workloads of the metric's family, each timed the same way and
+# reported as a sub-record of the one JSON line: the encoder without global
+# tokens (the band kernel alone: the shape the 50%-of-MFMA target is judged
+# on), the two autoregressive char-LM shapes, the QA batch with 64 global
+# tokens and the LED encoder.
+SUB_WORKLOADS = ["encoder_b2_h12_n4096_w512", "arlm_b1_h12_n8192_w512_causal_dil2",
+                 "arlm_b1_h8_n23040_w1024_causal_dil4", "qa_b4_h12_n4096_w512_g64",
+                 "led_b1_h12_n16384_w1024_g1"]
+
+
+def forward_record(name, steps, warmup, dev):
+    """One workload's forward: rotating input sets drawn on the device (the
+    workload's own distribution, N(0,1) * 0.125, at least 600 MB in all so
+    the Infinity Cache cannot hold them), the step time over ``steps`` forwards, the forward kernel's
+    and the merges' durations from HIP events, and the kernel's roofline
+    fractions (algorithmic bytes and FLOPs over the event-timed duration)."""
+    import torch
+
+    from sliding_window_attention_banded_amd import Plan
+    from sliding_window_attention_banded_amd.accounting import (
+        algorithmic_bytes, band_flops, useful_flops)
+    from sliding_window_attention_banded_amd.workloads import WORKLOADS, make_device_inputs
+
+    wl = WORKLOADS[name]
+    probe = make_device_inputs(wl, 1000, dev, "normal")
+    set_bytes = sum(t.numel() * t.element_size() for t in probe.values() if t is not None)
+    nsets = max(1, -(-600 * 2 ** 20 // set_bytes))
+    sets = [probe] + [make_device_inputs(wl, 1000 + s, dev, "normal") for s in range(1, nsets)]
+    outs = [torch.empty_like(x["q"]) for x in sets]
+    lses = [torch.empty((wl.batch, wl.heads, wl.n), dtype=torch.float32, device=dev) for _ in sets]
+    stream = torch.cuda.current_stream(dev)
+    with Plan(wl.batch, wl.heads, wl.n, wl.d, wl.window, wl.dilation, wl.causal,
+              wl.global_idx, wl.torch_dtype) as plan:
+        def run(k):
+            for i in range(k):
+                x = sets[i % nsets]
+                plan.forward(x["q"], x["k"], x["v"], x["qg"], x["kg"], x["vg"],
+                             out=outs[i % nsets], lse=lses[i % nsets], stream=stream)
+
+        run(warmup)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        plan.set_timing(True)
+        run(steps)
+        kms, mms, _ = plan.kernel_times()
+        plan.set_timing(False)
+    del sets, outs, lses
+    torch.cuda.empty_cache()
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    kfl, kby, bf = useful_flops(wl), algorithmic_bytes(wl), band_flops(wl)
+    sec = kms * 1e-3
+    hbm_frac = kby / sec / 1e9 / PEAK_HBM_GBS
+    mfma_frac = kfl / sec / 1e12 / peak
+    bound = "hbm" if kby / (PEAK_HBM_GBS * 1e9) >= kfl / (peak * 1e12) else "mfma"
+    rec = {"workload": name, "ms_per_step": ms, "value": bf / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+           "tokens_per_s": wl.batch * wl.n / (ms * 1e-3), "input_sets": nsets,
+           "kernel": "attn_fwd", "kernel_us": kms * 1e3, "merge_us": mms * 1e3,
+           "roofline": {"bound": bound, "frac": hbm_frac if bound == "hbm" else mfma_frac,
+                        "hbm_frac": hbm_frac, "mfma_frac": mfma_frac,
+                        "hbm_gbs": kby / sec / 1e9, "mfma_tflops": kfl / sec / 1e12,
+                        "algorithmic_bytes_per_launch": kby,
+                        "algorithmic_gflop_per_launch": kfl / 1e9}}
+    print(f"[bench] sub-record {name}: {ms * 1e3:.2f} us/step, kernel {kms * 1e3:.2f} us, "
+          f"MFMA {mfma_frac:.3f}, HBM {hbm_frac:.3f}", file=sys.stderr, flush=True)
+    return rec
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -159,6 +233,8 @@ def main():
                     help="skip the backward-pass measurement")
     ap.add_argument("--no-projection", action="store_true",
                     help="skip the projection-prologue measurement")
+    ap.add_argument("--no-sub-records", action="store_true",
+                    help="skip the other workloads' forward records")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -349,6 +425,12 @@ def main():
                 "gbs": pby / (pms * 1e-3) / 1e9, "hbm_frac": pby / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "bound": "mfma" if pfl / (PEAK_BF16_TFLOPS * 1e12) >= pby / (PEAK_HBM_GBS * 1e9) else "hbm"}
 
+    plan.close()
+    subs = None
+    if not args.no_sub_records:
+        subs = [forward_record(nm, min(args.steps, 100), min(args.warmup, 10), dev)
+                for nm in SUB_WORKLOADS if nm != wl.name]
+
     line = {
         "metric": METRIC,
         "value": bf / (ms * 1e-3) / 1e12,
@@ -372,9 +454,9 @@ def main():
         "roofline": roof,
         "backward": bwd,
         "projection": proj,
+        "workloads": subs,
         "cpu_baseline": None,
     }
-    plan.close()
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -79,8 +79,12 @@ typedef struct swattn_params {
 typedef struct swattn_plan swattn_plan;
 
 /*
- * Validate the parameters and build a plan: per-head (left, right, dilation)
- * table, the residue-class tile schedule of the band and its key split, the
+ * Validate the parameters and build a plan for the attention pattern of
+ * section 3-1 of the Longformer summary page: the per-head window ("Sliding
+ * Window") and dilation ("Dilated Sliding Window"), the global set ("Global
+ * Attention") and the left-only mask of section 7. The plan holds the
+ * per-head (left, right, dilation) table, the residue-class tile schedule of
+ * the band and its key split, the
  * sorted device copy of G (per item with global_offsets), and one device
  * allocation for every workspace the forward and backward use (global-row
  * partials, key-split partials, the backward's per-row statistics). Every
@@ -97,7 +101,11 @@ int swattn_create(const swattn_params* p, swattn_plan** out);
 
 /*
  * Enqueue one forward pass on `stream` (a hipStream_t; NULL = the default
- * stream) and return without waiting.
+ * stream) and return without waiting: O and LSE as defined at the top of this
+ * file (section 3-1 of the Longformer summary page, its four bullets, and
+ * section 7 for the causal mask), the band and the global columns from
+ * Q, K, V, the rows of G from Qg, Kg, Vg ("Linear Projections for Global
+ * Attention").
  *   q, k, v     device, [B, H, n, d] contiguous (d fastest), plan dtype;
  *   qg, kg, vg  device, same shape and dtype: the separate global projections
  *               (only rows G of qg are read; kg, vg are read in full). They
@@ -196,8 +204,10 @@ int swattn_project(const void* x, const void* w, const void* bias, void* out,
                    void* stream);
 
 /*
- * Free the plan and its device memory. NULL is a no-op. The caller must make
- * sure no enqueued forward still uses the plan (e.g. synchronise its stream).
+ * Free the plan (the pattern tables of section 3-1 that swattn_create built,
+ * and its workspaces) and its device memory. NULL is a no-op. The caller must
+ * make sure no enqueued forward still uses the plan (e.g. synchronise its
+ * stream).
  */
 int swattn_destroy(swattn_plan* plan);
 
@@ -221,7 +231,8 @@ int swattn_kernel_times(swattn_plan* plan, float* band_ms, float* global_ms, int
 /* Static, human-readable name of a status code. */
 const char* swattn_status_string(int status);
 
-/* Message of the last error raised on this host thread ("" when none). */
+/* Message of the last error raised on this host thread ("" when none):
+ * the HIP runtime's error text for SWATTN_ERR_HIP, else the failed check. */
 const char* swattn_last_error(void);
 
 #ifdef __cplusplus

@@ -172,18 +172,24 @@ def make_inputs(wl: Workload, seed: int, kind: str = "normal"):
     return out
 
 
-def make_device_inputs(wl: Workload, seed: int, device):
-    """The "sharp" distribution of make_inputs (q, k ~ N(0,1) * 2, v ~ U(-1, 1);
-    qg, kg, vg likewise when the workload has global tokens), drawn directly
-    on ``device`` with its own seeded generator: for shapes too large to draw
-    on the host (several GB per tensor). Rounded to nearest-even into the
-    workload dtype."""
+def make_device_inputs(wl: Workload, seed: int, device, kind: str = "sharp"):
+    """The "sharp" (q, k ~ N(0,1) * 2, v ~ U(-1, 1)) or "normal" (every
+    tensor N(0,1) * scale) distribution of make_inputs, for q, k, v and, when
+    the workload has global tokens, qg, kg, vg, drawn directly on ``device``
+    with its own seeded generator: for shapes too large to draw on the host
+    (several GB per tensor) and for benchmark input sets. Rounded to
+    nearest-even into the workload dtype. (The draws differ from
+    make_inputs', which come from a CPU generator.)"""
+    if kind not in ("normal", "sharp"):
+        raise ValueError(kind)
     gen = torch.Generator(device=device).manual_seed(int(seed))
     shape = (wl.batch, wl.heads, wl.n, wl.d)
     out = {}
     roles = ["q", "k", "v"] + (["qg", "kg", "vg"] if has_globals(wl) else [])
     for r in roles:
-        if r in ("v", "vg"):
+        if kind == "normal":
+            t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * wl.scale
+        elif r in ("v", "vg"):
             t = torch.rand(shape, generator=gen, device=device, dtype=torch.float32) * 2.0 - 1.0
         else:
             t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * 2.0
