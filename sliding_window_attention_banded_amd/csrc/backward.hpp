@@ -380,15 +380,26 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   }
   wait_vmcnt<0>();
 
-  if (wave_live && row_ok) {
-    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dq) + roff), w.dq, p.scale, g);
-    // dQg is zero off G (rows of G, log2-LSE +inf, come from bwd_gred)
-    if (p.dqg && w.lse2 != __builtin_inff()) {
-      __bf16* zrow = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dqg) + roff);
+  if (wave_live) {
+    // whole-row stores through the stage of ring step nband (free: see the
+    // forward's band blocks)
+    const int sa = nband % 3;
+    char* slot = (sa == 0 ? st0 : (sa == 1 ? st1 : st2)) + 4096 * wave;
+    store_o_rows(slot, reinterpret_cast<char*>(p.dq) + base, w.dq.a, p.scale, lane, qw0, nr, r, dil);
+    // dQg is zero off G (rows of G, log2-LSE +inf, come from bwd_gred): lane
+    // i writes 16 bytes of row 8k + i/8, whose log2-LSE lane 8k + i/8 holds
+    if (p.dqg) {
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) *reinterpret_cast<uint2*>(zrow + 32 * dh + 8 * a + 4 * g) = uint2{0, 0};
+      for (int k = 0; k < 4; ++k) {
+        const int row = 8 * k + (lane >> 3);
+        const float l2 = __shfl(w.lse2, row);
+        if (qw0 + row < nr && l2 != __builtin_inff())
+          __builtin_nontemporal_store(
+              u32x4{0u, 0u, 0u, 0u},
+              reinterpret_cast<u32x4*>(reinterpret_cast<char*>(p.dqg) + base +
+                                       (long)(r + (qw0 + row) * dil) * ROWB + (lane & 7) * 16));
+      }
     }
   }
 }
@@ -526,9 +537,13 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
   }
   wait_vmcnt<0>();
 
-  if (wave_live && key_ok) {
-    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dk) + roff), w.dk, p.scale, g);
-    store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dv) + roff), w.dv, 1.0f, g);
+  if (wave_live) {
+    // whole-row stores through the stage of ring step nband, dK then dV (one
+    // wave's LDS accesses stay in order)
+    const int sa = nband % 3;
+    char* slot = (sa == 0 ? st0 : (sa == 1 ? st1 : st2)) + 4096 * wave;
+    store_o_rows(slot, reinterpret_cast<char*>(p.dk) + base, w.dk.a, p.scale, lane, kw0, nr, r, dil);
+    store_o_rows(slot, reinterpret_cast<char*>(p.dv) + base, w.dv.a, 1.0f, lane, kw0, nr, r, dil);
   }
 }
 

@@ -497,6 +497,42 @@ DEV void store_o(float* orow, const WaveAcc& acc, float inv, int g) {
     }
 }
 
+// Store a wave's 32 rows of 64 (an O, dQ, dK or dV accumulator, times `inv`,
+// in bf16) so that every store instruction writes whole 128-byte rows, with
+// non-temporal stores: the two lanes of row l put their halves into `slot` (4 KB of LDS that only this wave uses;
+// 16-byte chunks permuted by the row's low bits against bank conflicts),
+// then each lane reads back one 16-byte chunk of row 8k + lane/8 and stores
+// it. Written this way the rows stream out past L2 instead of being left
+// dirty for the write-back at the kernel's end. Row qw0 + i sits at
+// position r + (qw0 + i) * dil; rows qw0 + i >= nr are skipped.
+DEV void store_o_rows(char* slot, char* obase, const f32x16 (&o)[2], float inv, int lane, int qw0,
+                      int nr, int r, int dil) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  lds_char* s = (lds_char*)slot;
+  const int l = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(o[dh][4 * a + e] * inv);
+      const int pc = (4 * dh + a) ^ (l & 7);  // chunk 4dh+a holds d = 32dh+8a .. +7
+      *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(s + l * 128 + pc * 16 + g * 8) = t;
+    }
+  // the same wave reads what it wrote: LDS keeps one wave's accesses in order
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = 8 * k + (lane >> 3), ch = lane & 7;
+    const u32x4 v =
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + row * 128 + ((ch ^ (row & 7)) << 4));
+    const int qi = qw0 + row;
+    if (qi < nr)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (long)(r + qi * dil) * 128 + ch * 16));
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Tile movement.
 
@@ -1002,6 +1038,16 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
       float* rec = p.part + (((long)bh * p.n + pos_q) * p.parts + part) * PART_STRIDE;
       store_o(rec, acc, 1.0f, g);
       if (g == 0) *reinterpret_cast<f32x2*>(rec + HD) = f32x2{acc.m, ltot};
+    } else if (BF16 && c.nband > 0) {
+      // The stage of ring step nband takes the rows: nobody reads it again,
+      // and every wave's loads into it completed before the last ring
+      // barrier (issued at step nband-2, or by ring_start when nband = 1,
+      // and waited for at step nband-1 or before the ring). Each wave uses
+      // the 4 KB at 4096 * wave.
+      const int sa = c.nband % 3;
+      char* slot = (sa == 0 ? st0 : (sa == 1 ? st1 : st2)) + 4096 * wave;
+      store_o_rows(slot, reinterpret_cast<char*>(p.o) + base, acc.o, 1.0f / ltot, lane, qw0, nr, r, dil);
+      if (row_ok && p.lse && g == 0) p.lse[(long)bh * p.n + pos_q] = acc.m * p.scale + __logf(ltot);
     } else if (row_ok) {
       const float inv = 1.0f / ltot;
       T* orow = reinterpret_cast<T*>(reinterpret_cast<char*>(p.o) + base + (long)pos_q * ROWB);
