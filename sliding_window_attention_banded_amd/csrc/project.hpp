@@ -67,6 +67,14 @@ struct ProjParams {
 DEV int pj_phys(int row, int ch) { return ch ^ ((row >> 2) & 3); }
 DEV int pj_off(int row, int ch) { return row * PJ_ROWB + (pj_phys(row, ch) << 4); }
 
+// 16 bytes of an output row, non-temporal: the rows are written whole (eight
+// lanes per 128-byte row) and stream out past L2 instead of staying dirty
+// there until the kernel's end.
+DEV void store_row16(__bf16* dst, const uint4& v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+}
+
 // Block -> (token tile, feature tile). xcd_remap gives each XCD a contiguous
 // range of the order; the order runs over groups of PJ_GROUP token tiles and,
 // within a group, feature-tile-major, so the blocks an XCD runs together
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) 
     }
 #pragma unroll
     for (int it = 0; it < C::WT / 8; ++it)
-      *reinterpret_cast<uint4*>(orow + (size_t)(it * 8 + (lane >> 3)) * 64 + (lane & 7) * 8) = v[it];
+      store_row16(orow + (size_t)(it * 8 + (lane >> 3)) * 64 + (lane & 7) * 8, v[it]);
     return;
   }
 #pragma unroll
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) 
     if (tok < p.M) {
       int b = item0, i = pos0 + row;
       if (!one_item) { b = tok / p.n; i = tok - b * p.n; }
-      *reinterpret_cast<uint4*>(obase + b * item_stride + (size_t)i * 64 + c * 8) = v;
+      store_row16(obase + b * item_stride + (size_t)i * 64 + c * 8, v);
     }
   }
 }
