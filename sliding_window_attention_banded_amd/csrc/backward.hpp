@@ -644,7 +644,7 @@ DEV void bwd_gq_block(const BwdParams& p, int gb, char* st0, char* st1, char* st
 
 constexpr int GKV_GROUPS = 4;
 
-DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
+DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, char* st1, int* gpos) {
   constexpr int ROWB = ElemTraits<__bf16>::ROWB;
   constexpr int TILEB = KT * ROWB;
   const int tid = threadIdx.x;
@@ -685,7 +685,6 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
     const int kw0 = k0 + 32 * wave;
     const bool wave_live = kw0 < p.n;
     const int kj = kw0 + (lane & 31);
-    const bool key_ok = kj < p.n;
     const int pos_k = min(kj, p.n - 1);
     const long roff = base + (long)pos_k * ROWB;
     DkvWave w;
@@ -708,9 +707,11 @@ DEV void bwd_gkv_block(const BwdParams& p, int blk, char* st0, int* gpos) {
         }
       }
     }
-    if (wave_live && key_ok) {
-      store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dkg) + roff), w.dk, p.scale, g);
-      store_row(reinterpret_cast<__bf16*>(reinterpret_cast<char*>(p.dvg) + roff), w.dv, 1.0f, g);
+    if (wave_live) {
+      // whole-row stores staged in st1, which this block does not use
+      char* slot = st1 + 4096 * wave;
+      store_o_rows(slot, reinterpret_cast<char*>(p.dkg) + base, w.dk.a, p.scale, lane, kw0, p.n, 0, 1);
+      store_o_rows(slot, reinterpret_cast<char*>(p.dvg) + base, w.dv.a, 1.0f, lane, kw0, p.n, 0, 1);
     }
   }
 }
@@ -894,7 +895,7 @@ __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
   b -= p.n_gcol;
   if (b < p.n_gq) { bwd_gq_block(p, b, st0, st1, st2); return; }
   b -= p.n_gq;
-  if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, gmeta[0]); return; }
+  if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, st1, gmeta[0]); return; }
   b -= p.n_gkv;
   if (b < p.nq) { bwd_dq_block(p, xcd_remap(b, p.nq), st0, st1, st2, gmeta); return; }
   b -= p.nq;
