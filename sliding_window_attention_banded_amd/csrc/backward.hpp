@@ -94,23 +94,25 @@ constexpr int GCOL_QC_MAX = 4096;
 constexpr int GQ_KEYS_SMALL_G = 1024;
 
 // ----------------------------------------------------------------------------
-// Row statistics: 8 lanes per row, 8 elements each.
+// Row statistics: 4 lanes per row, 16 elements (two 16-byte loads) each.
 
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
   const long t = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = t >> 3;
-  const int part = threadIdx.x & 7;
+  const long row = t >> 2;
+  const int part = threadIdx.x & 3;
   float acc = 0.f;
   if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.o) + row * HD + 8 * part);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.dout) + row * HD + 8 * part);
+    const bf16x8* ap = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.o) + row * HD + 16 * part);
+    const bf16x8* bp = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.dout) + row * HD + 16 * part);
+    const bf16x8 a0 = ap[0], a1 = ap[1], b0 = bp[0], b1 = bp[1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a0[e], (float)b0[e], acc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a1[e], (float)b1[e], acc);
   }
-  // sum the 8 lanes of the row (aligned groups of 8 within the wave)
+  // sum the 4 lanes of the row (aligned groups of 4 within the wave)
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
   const long rowc = row < rows ? row : rows - 1;
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, (int)(rowc / p.n / p.H));
   if (row < rows && part == 0) {

@@ -708,7 +708,7 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   bp.n_gkv = pl->n_gkv; bp.n_gcol = pl->n_gcol;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   const long rows = (long)pl->B * pl->H * pl->n;
-  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, st, bp, rows);
+  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0, st, bp, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch bwd_prep");
   hipLaunchKernelGGL(bwd_main, dim3(2 * bp.nq + bp.n_gq + bp.n_gkv + bp.n_gcol), dim3(256), 0, st, bp);
