@@ -213,12 +213,13 @@ int swattn_destroy(swattn_plan* plan);
 
 /*
  * Measurement hooks (not part of the computation). With timing enabled, each
- * forward's kernels are launched with start/stop HIP events that the runtime
- * records at the kernel's own start and end on the forward's stream, in two
+ * forward records HIP events on its stream around its kernels, in two
  * phases: the forward kernel (band rows, global columns and the global rows'
  * partials), and the merges after it (the key-part merge with a key split,
- * the global-row merge with global tokens; from the first one's start to the
- * last one's end, 0 when there are none); up to 4096 forwards are kept.
+ * the global-row merge with global tokens; from before the first one to
+ * after the last one, 0 when there are none). An interval covers the
+ * kernels' dispatch and completion, including the cache write-back at a
+ * kernel's end; up to 4096 forwards are kept.
  * swattn_kernel_times() waits for the recorded events, returns the average
  * duration in milliseconds of each phase over the recorded forwards and the
  * number of forwards averaged, then clears the record. Enabling creates the
