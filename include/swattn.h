@@ -183,20 +183,22 @@ int swattn_backward(swattn_plan* plan, const void* q, const void* k, const void*
  * batch item b and feature e < 64:
  *   out[p][b][h][i][e] = sum_c x[b][i][c] * w[(p*heads + h)*64 + e][c]
  *                        + bias[(p*heads + h)*64 + e]
- * accumulated in fp32, rounded once to bf16.
- *   x     device bf16 [batch, n, d_model] contiguous;
- *   w     device bf16 [nproj*heads*64, d_model]: one output feature per row,
+ * accumulated in fp32 and, for bf16, rounded once to bf16. x, w, bias and
+ * out all have the type `dtype` (SWATTN_BF16: the matrix cores; SWATTN_FP32:
+ * the vector ALUs, a plain fp32 dot product in input-feature order).
+ *   x     device [batch, n, d_model] contiguous;
+ *   w     device [nproj*heads*64, d_model]: one output feature per row,
  *         the layout of a linear layer's weight; the rows of projection p
  *         are the block p*heads*64 .. (p+1)*heads*64-1, head-major;
- *   bias  device bf16 [nproj*heads*64] or NULL (no bias);
- *   out   device bf16 [nproj, batch, heads, n, 64], written in full: out + p*
+ *   bias  device [nproj*heads*64] or NULL (no bias);
+ *   out   device [nproj, batch, heads, n, 64], written in full: out + p*
  *         batch*heads*n*64 elements is projection p in the [B, H, n, d]
  *         layout swattn_forward reads (order q, k, v, then qg, kg, vg);
  *         must not overlap an input.
  * d_model must be a multiple of 32 and x, w each smaller than 2 GiB; every
  * device pointer 16-byte aligned. The caller owns every buffer; nothing is
  * allocated. Errors: INVALID_ARG (NULL pointer, size < 1, out overlapping an
- * input), UNSUPPORTED (dtype other than SWATTN_BF16, d_model, sizes),
+ * input), UNSUPPORTED (unknown dtype, d_model, sizes),
  * ALIGNMENT, HIP (launch failure).
  */
 int swattn_project(const void* x, const void* w, const void* bias, void* out,

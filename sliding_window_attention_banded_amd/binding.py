@@ -262,18 +262,21 @@ class Plan:
 
 def project(x, weight, bias=None, heads=None, out=None, stream=None):
     """Enqueue the projections in front of the attention (swattn_project):
-    x [B, n, d_model] bf16, weight [P*heads*64, d_model] bf16 (a linear
-    layer's layout), bias [P*heads*64] bf16 or None. Returns out
-    [P, B, heads, n, 64]; out[p] is projection p (q, k, v, then qg, kg, vg)
-    in the layout Plan.forward takes."""
+    x [B, n, d_model], weight [P*heads*64, d_model] (a linear layer's
+    layout), bias [P*heads*64] or None, all bf16 or all fp32. Returns out
+    [P, B, heads, n, 64] of the same dtype; out[p] is projection p (q, k, v,
+    then qg, kg, vg) in the layout Plan.forward takes."""
     lib = load_library()
     if heads is None or heads < 1:
         raise SwattnError(ERR_INVALID_ARG, "heads must be given and >= 1")
+    dt = x.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise SwattnError(ERR_INVALID_ARG, "x must be bf16 or fp32")
     for name, t in (("x", x), ("weight", weight), ("bias", bias)):
         if t is None and name == "bias":
             continue
-        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise SwattnError(ERR_INVALID_ARG, f"{name} must be a contiguous bf16 device tensor")
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise SwattnError(ERR_INVALID_ARG, f"{name} must be a contiguous {dt} device tensor like x")
     if x.dim() != 3 or weight.dim() != 2 or weight.shape[1] != x.shape[2] \
             or weight.shape[0] % (heads * 64) or weight.shape[0] == 0:
         raise SwattnError(ERR_INVALID_ARG, "need x [B, n, D] and weight [P*heads*64, D]")
@@ -283,13 +286,14 @@ def project(x, weight, bias=None, heads=None, out=None, stream=None):
         raise SwattnError(ERR_INVALID_ARG, "bias must be [P*heads*64]")
     shape = (P, B, heads, n, 64)
     if out is None:
-        out = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
-    elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise SwattnError(ERR_INVALID_ARG, f"out must be contiguous bf16 of shape {shape}")
+        out = torch.empty(shape, dtype=dt, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != dt or not out.is_contiguous() or not out.is_cuda:
+        raise SwattnError(ERR_INVALID_ARG, f"out must be a contiguous {dt} device tensor of shape {shape}")
     st = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(lib, lib.swattn_project(x.data_ptr(), weight.data_ptr(),
                                    bias.data_ptr() if bias is not None else None,
-                                   out.data_ptr(), B, n, D, heads, P, BF16,
+                                   out.data_ptr(), B, n, D, heads, P,
+                                   BF16 if dt == torch.bfloat16 else FP32,
                                    ctypes.c_void_p(st.cuda_stream)),
            "swattn_project")
     return out

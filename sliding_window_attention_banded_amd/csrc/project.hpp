@@ -286,4 +286,73 @@ __global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) 
   }
 }
 
+// ----------------------------------------------------------------------------
+// fp32 projections: the same map and output layout with x, w, bias and out
+// in fp32, for the fp32 attention path. On the vector ALUs (fp32 FMAs in
+// input-feature order, so the result is a plain fp32 dot product): a
+// workgroup computes 64 tokens x one 64-feature (projection, head) block,
+// staging 16 input features of x and w at a time in LDS; each thread owns
+// 4 tokens x 4 features.
+
+struct ProjParamsF32 {
+  const float* x;     // [M][D]
+  const float* w;     // [N][D]
+  const float* bias;  // [N] or NULL
+  float* out;         // [P][B][H][n][64]
+  int M, N, D, n, B, H;
+  int nph;            // N / 64 feature blocks
+};
+
+__global__ __launch_bounds__(256) void proj_f32(ProjParamsF32 p) {
+  constexpr int TT = 64, TK = 16;
+  __shared__ float xs[TK][TT + 4];  // [input feature][token]
+  __shared__ float ws[TK][TT + 4];  // [input feature][output feature]
+  const int ph = blockIdx.x % p.nph, tm = blockIdx.x / p.nph;
+  const int tok0 = tm * TT, f0 = ph * HD;
+  const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < p.D; k0 += TK) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, row = idx >> 4, kk = idx & 15;
+      const int tok = min(tok0 + row, p.M - 1);  // rows past M are computed, never stored
+      xs[kk][row] = p.x[(long)tok * p.D + k0 + kk];
+      ws[kk][row] = p.w[(long)(f0 + row) * p.D + k0 + kk];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[kk][4 * ti + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[kk][4 * tj + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const int proj = ph / p.H, h = ph - proj * p.H;
+  float bj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bj[j] = p.bias ? p.bias[f0 + 4 * tj + j] : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = tok0 + 4 * ti + i;
+    if (tok >= p.M) continue;
+    const int b = tok / p.n, pos = tok - b * p.n;
+    float* orow = p.out + ((((size_t)proj * p.B + b) * p.H + h) * p.n + pos) * HD;
+    f32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = acc[i][j] + bj[j];
+    *reinterpret_cast<f32x4*>(orow + 4 * tj) = v;
+  }
+}
+
 }  // namespace swattn

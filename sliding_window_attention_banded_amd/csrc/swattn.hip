@@ -728,17 +728,34 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   if (!x || !w || !out) return fail(SWATTN_ERR_INVALID_ARG, "x, w and out must not be NULL");
   if (batch < 1 || n < 1 || heads < 1 || nproj < 1 || d_model < 1)
     return fail(SWATTN_ERR_INVALID_ARG, "batch, n, heads, nproj and d_model must be >= 1");
-  if (dtype != SWATTN_BF16) return fail(SWATTN_ERR_UNSUPPORTED, "the projection is bf16 only");
+  if (dtype != SWATTN_BF16 && dtype != SWATTN_FP32) return fail(SWATTN_ERR_UNSUPPORTED, "unknown dtype");
   if (d_model % PJ_TK) return fail(SWATTN_ERR_UNSUPPORTED, "d_model must be a multiple of 32");
   const long M = (long)batch * n, N = (long)nproj * heads * HD;
+  const long es = dtype == SWATTN_BF16 ? 2 : 4;  // element size
   // 32-bit byte offsets into x and w
-  if (M * d_model * 2 >= (1L << 31) || N * d_model * 2 >= (1L << 31))
+  if (M * d_model * es >= (1L << 31) || N * d_model * es >= (1L << 31))
     return fail(SWATTN_ERR_UNSUPPORTED, "x and w must each be smaller than 2 GiB");
   for (const void* ptr : {x, w, bias, (const void*)out})
     if (ptr && !aligned16(ptr)) return fail(SWATTN_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  const size_t xb = (size_t)M * d_model * 2, wb = (size_t)N * d_model * 2, ob = (size_t)M * N * 2;
-  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, bias, (size_t)N * 2))
+  const size_t xb = (size_t)M * d_model * es, wb = (size_t)N * d_model * es, ob = (size_t)M * N * es;
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, w, wb) || overlaps(out, ob, bias, (size_t)N * es))
     return fail(SWATTN_ERR_INVALID_ARG, "out overlaps an input");
+  if (dtype == SWATTN_FP32) {
+    const long ntm = (M + 63) / 64;
+    if (ntm * (N / HD) > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+    ProjParamsF32 pf;
+    pf.x = static_cast<const float*>(x);
+    pf.w = static_cast<const float*>(w);
+    pf.bias = static_cast<const float*>(bias);
+    pf.out = static_cast<float*>(out);
+    pf.M = (int)M; pf.N = (int)N; pf.D = d_model; pf.n = n; pf.B = batch; pf.H = heads;
+    pf.nph = (int)(N / HD);
+    hipLaunchKernelGGL(proj_f32, dim3((unsigned)(ntm * pf.nph)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), pf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch proj_f32");
+    return SWATTN_OK;
+  }
   int cus = 256;
   {
     int dev = 0;

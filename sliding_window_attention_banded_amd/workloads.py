@@ -200,17 +200,20 @@ def make_device_inputs(wl: Workload, seed: int, device, kind: str = "sharp"):
     return out
 
 
-def make_projection_inputs(batch, n, d_model, heads, nproj, seed, bias=True):
-    """Seeded CPU bf16 tensors for the projections in front of the attention:
+def make_projection_inputs(batch, n, d_model, heads, nproj, seed, bias=True, dtype="bf16"):
+    """Seeded CPU tensors for the projections in front of the attention:
     x [batch, n, d_model] ~ N(0, 1) (a normalised layer input), weight
     [nproj*heads*64, d_model] ~ N(0, 1/d_model) (the usual fan-in scaling,
     so that the projections come out of order one) and bias
     [nproj*heads*64] ~ N(0, 0.1^2) or None. Draw order: x, weight, bias;
-    drawn in float32, rounded to nearest-even bf16."""
+    drawn in float32 and, for dtype "bf16", rounded to nearest-even bf16."""
+    if dtype not in ("bf16", "fp32"):
+        raise ValueError(dtype)
     gen = torch.Generator(device="cpu").manual_seed(20_000 + int(seed))
     N = nproj * heads * 64
     x = torch.randn((batch, n, d_model), generator=gen, dtype=torch.float32)
     w = torch.randn((N, d_model), generator=gen, dtype=torch.float32) / d_model ** 0.5
     b = torch.randn((N,), generator=gen, dtype=torch.float32) * 0.1 if bias else None
-    bf = lambda t: None if t is None else t.to(torch.bfloat16).contiguous()
-    return bf(x), bf(w), bf(b)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cv = lambda t: None if t is None else t.to(tdt).contiguous()
+    return cv(x), cv(w), cv(b)

@@ -127,7 +127,7 @@ static int more_invalid(void) {
     bad |= expect(swattn_project(base, base + 0x10000, NULL, base + 0x20000, 1, 64, 48, 1, 3,
                                  SWATTN_BF16, NULL), SWATTN_ERR_UNSUPPORTED, "project d_model 48");
     bad |= expect(swattn_project(base, base + 0x10000, NULL, base + 0x20000, 1, 64, 64, 1, 3,
-                                 SWATTN_FP32, NULL), SWATTN_ERR_UNSUPPORTED, "project fp32");
+                                 7, NULL), SWATTN_ERR_UNSUPPORTED, "project dtype 7");
     bad |= expect(swattn_project(base + 1, base + 0x10000, NULL, base + 0x20000, 1, 64, 64, 1, 3,
                                  SWATTN_BF16, NULL), SWATTN_ERR_ALIGNMENT, "project misaligned x");
     bad |= expect(swattn_project(base, base + 0x10000, NULL, base + 0x100, 1, 64, 64, 1, 3,

@@ -88,7 +88,7 @@ _X, _W, _O = 0x100000, 0x800000, 0x4000000
     (dict(x=None), 1), (dict(w=None), 1), (dict(out=None), 1),
     (dict(batch=0), 1), (dict(n=0), 1), (dict(heads=0), 1), (dict(nproj=0), 1),
     (dict(d_model=0), 1),
-    (dict(dtype=1), 2), (dict(d_model=80), 2),
+    (dict(dtype=7), 2), (dict(d_model=80), 2),
     (dict(batch=1 << 20, n=1 << 10), 2),   # x of 2^30 * 64 * 2 bytes
     (dict(x=_X + 8), 4), (dict(bias=_W + 0x10000 + 8), 4), (dict(out=_O + 2), 4),
     (dict(out=_X + 64), 1),                # out overlaps x

@@ -110,10 +110,10 @@ def test_project_then_attention_matches_the_oracle_chain():
     assert err <= 2e-2 and lerr <= 2e-2
 
 
-def test_project_rejects_fp32_and_bad_shapes():
+def test_project_rejects_fp16_and_bad_shapes():
     from sliding_window_attention_banded_amd import SwattnError, project
-    x = torch.zeros((1, 8, 64), dtype=torch.float32, device="cuda")
-    w = torch.zeros((192, 64), dtype=torch.float32, device="cuda")
+    x = torch.zeros((1, 8, 64), dtype=torch.float16, device="cuda")
+    w = torch.zeros((192, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(SwattnError):
         project(x, w, heads=1)
     with pytest.raises(SwattnError):
@@ -157,3 +157,67 @@ def test_project_random_shapes(B, n, D, H, P, bias):
     out = project(x.cuda(), w.cuda(), b.cuda() if b is not None else None, heads=H)
     torch.cuda.synchronize()
     _check(out, x, w, b, H, f"rand B{B}n{n}D{D}H{H}P{P}")
+
+
+# fp32 projections: no final rounding, so the bound is the accumulation's
+# alone, |got - ref| <= E = 4 (D+1) 2^-24 A per element, with A as above
+# (the vector-ALU kernel sums in input-feature order with fp32 FMAs, whose
+# error is at most (D+1) 2^-24 A; 4x as margin).
+CASES_F32 = [
+    (1, 300, 128, 2, 3, True),
+    (2, 777, 192, 3, 6, False),
+    (1, 1, 64, 1, 1, True),
+    (2, 256, 1024, 1, 2, True),
+]
+
+
+@pytest.mark.parametrize("B,n,D,H,P,bias", CASES_F32,
+                         ids=[f"f32_B{c[0]}_n{c[1]}_D{c[2]}_H{c[3]}_P{c[4]}" for c in CASES_F32])
+def test_project_fp32(B, n, D, H, P, bias):
+    from oracle import project as oracle_project
+    from sliding_window_attention_banded_amd import project
+    print(f"[proj-f32] B{B} n{n} D{D} H{H} P{P} bias={bias}", flush=True)
+    x, w, b = make_projection_inputs(B, n, D, H, P, 3, bias, dtype="fp32")
+    out = project(x.cuda(), w.cuda(), b.cuda() if b is not None else None, heads=H)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32
+    x64, w64 = to64(x), to64(w)
+    b64 = to64(b) if b is not None else None
+    refs = oracle_project(x64, w64, b64, H)
+    absd = oracle_project(np.abs(x64), np.abs(w64), np.abs(b64) if b64 is not None else None, H)
+    g = out.double().cpu().numpy()
+    for p, (ref, a) in enumerate(zip(refs, absd)):
+        e = 4.0 * (D + 1) * 2.0 ** -24 * a
+        err = np.abs(g[p] - ref)
+        worst = float((err / (e + 1e-30)).max())
+        print(f"  p{p}: max err {err.max():.3e}, worst err/bound {worst:.3f}", flush=True)
+        assert np.isfinite(g[p]).all()
+        assert worst <= 1.0, f"p{p}: error above the fp32 bound"
+
+
+def test_project_rejects_mixed_dtypes():
+    from sliding_window_attention_banded_amd import SwattnError, project
+    x, w, b = make_projection_inputs(1, 64, 64, 1, 1, 0, True, dtype="fp32")
+    with pytest.raises(SwattnError):
+        project(x.cuda(), w.cuda().to(torch.bfloat16), b.cuda(), heads=1)
+
+
+def test_project_then_attention_fp32_chain():
+    """The fp32 path end to end: x -> fp32 projections -> fp32 banded
+    attention with a global token, against the oracle's float64 projections
+    fed to its attention, at the fp32 tolerance of the attention (1e-5)."""
+    from oracle import attention, project as oproject
+    from sliding_window_attention_banded_amd import Plan, project
+    B, n, D, H = 1, 512, 128, 2
+    win, dil, G = (64, 32), (1, 2), (0, 300)
+    x, w, b = make_projection_inputs(B, n, D, H, 6, 4, True, dtype="fp32")
+    qkv = project(x.cuda(), w.cuda(), b.cuda(), heads=H)
+    with Plan(B, H, n, 64, win, dil, False, G, torch.float32) as pl:
+        o, lse = pl.forward(*(qkv[i] for i in range(6)), want_lse=True)
+    torch.cuda.synchronize()
+    t = oproject(to64(x), to64(w), to64(b), H)
+    ro, rl = attention(*t, window=list(win), dilation=list(dil), causal=False, global_idx=list(G))
+    err = np.abs(o.double().cpu().numpy() - ro).max()
+    lerr = np.abs(lse.double().cpu().numpy() - rl).max()
+    print(f"  fp32 chain: O max-abs {err:.3e}, LSE max-abs {lerr:.3e}", flush=True)
+    assert err <= 1e-5 and lerr <= 1e-5
