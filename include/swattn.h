@@ -166,8 +166,12 @@ int swattn_forward_noalloc(const swattn_params* p, const void* q, const void* k,
  *                     when n_global == 0.
  * Gradients must not overlap each other or any input. The plan's workspace
  * holds per-row statistics, so a plan runs one backward (or forward) at a
- * time. bf16 plans only; the current HIP device must be the plan's.
- * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (fp32 plan), HIP.
+ * time. bf16 plans run on the matrix cores (P and dS enter their products
+ * in bf16); fp32 plans run an fp32 path on the vector ALUs, one wavefront
+ * per row for dq, dqg and one per key position for dk, dv, dkg, dvg, for
+ * correctness rather than speed. Tensors have the plan's dtype; the
+ * current HIP device must be the plan's.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 int swattn_backward(swattn_plan* plan, const void* q, const void* k, const void* v,
                     const void* qg, const void* kg, const void* vg, const void* o,

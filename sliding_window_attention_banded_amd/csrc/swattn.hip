@@ -15,6 +15,7 @@
 #include "swattn.h"
 #include "kernels.hpp"
 #include "backward.hpp"
+#include "backward_f32.hpp"
 #include "project.hpp"
 
 using namespace swattn;
@@ -282,7 +283,8 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const size_t sz_po = al(sizeof(float) * HD * nslot);
   const size_t sz_pml = al(sizeof(float) * 2 * nslot);
   const bool bwd = pl->dtype == SWATTN_BF16;
-  const size_t sz_stat = bwd ? al(sizeof(float) * (size_t)bh * p->n) : 0;
+  // per-row backward statistics (both dtypes; the fp32 backward uses D only)
+  const size_t sz_stat = al(sizeof(float) * (size_t)bh * p->n);
   const bool bwd_g = bwd && pl->ng > 0;
   pl->ngp = bwd_g ? (pl->ng + KT - 1) / KT * KT : 0;
   pl->ng32 = bwd_g ? (pl->ng + 31) / 32 * 32 : 0;
@@ -340,7 +342,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
     e = hipMemcpy(pl->bwd_glse2, inf.data(), sizeof(float) * inf.size(), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(pl->bwd_gdd, zero.data(), sizeof(float) * zero.size(), hipMemcpyHostToDevice);
   }
-  if (e == hipSuccess && bwd) {
+  if (e == hipSuccess) {
     std::vector<HeadGeom> hg(p->heads);
     for (int h = 0; h < p->heads; ++h) hg[h] = HeadGeom{half[h], p->causal ? 0 : half[h], dil[h], 0};
     e = hipMemcpy(pl->bwd_heads, hg.data(), sizeof(HeadGeom) * hg.size(), hipMemcpyHostToDevice);
@@ -661,7 +663,6 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
                                void* dqg, void* dkg, void* dvg, void* stream) {
   g_last_error.clear();
   if (!pl) return fail(SWATTN_ERR_INVALID_ARG, "plan must not be NULL");
-  if (pl->dtype != SWATTN_BF16) return fail(SWATTN_ERR_UNSUPPORTED, "the backward pass is bf16 only");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(SWATTN_ERR_INVALID_ARG, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
   if (const int rc = check_device(pl)) return rc;
@@ -673,7 +674,7 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   const void* all[] = {q, k, v, qg, kg, vg, o, lse, dout, dq, dk, dv, dqg, dkg, dvg};
   for (const void* x : all)
     if (x && !aligned16(x)) return fail(SWATTN_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  const size_t nbytes = (size_t)pl->B * pl->H * pl->n * HD * 2;
+  const size_t nbytes = (size_t)pl->B * pl->H * pl->n * HD * (pl->dtype == SWATTN_BF16 ? 2 : 4);
   const size_t lb = (size_t)pl->B * pl->H * pl->n * sizeof(float);
   const void* ins[] = {q, k, v, qg, kg, vg, o, dout};
   void* outs[] = {dq, dk, dv, dqg, dkg, dvg};
@@ -707,6 +708,19 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   bp.n_gkv = pl->n_gkv; bp.n_gcol = pl->n_gcol;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   const long rows = (long)pl->B * pl->H * pl->n;
+  if (pl->dtype == SWATTN_FP32) {
+    // the fp32 path: D, then dq/dqg per row and dk/dv/dkg/dvg per key
+    hipLaunchKernelGGL(bwd_f32_prep, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, bp, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch bwd_f32_prep");
+    hipLaunchKernelGGL(bwd_f32_rows, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, bp, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch bwd_f32_rows");
+    hipLaunchKernelGGL(bwd_f32_keys, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, bp, rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch bwd_f32_keys");
+    return SWATTN_OK;
+  }
   hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0, st, bp, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch bwd_prep");

@@ -37,7 +37,7 @@ FLOOR = 1e-6
 
 def cotangent(wl, seed):
     g = torch.Generator().manual_seed(10_000 + seed)
-    return torch.randn((wl.batch, wl.heads, wl.n, wl.d), generator=g).to(torch.bfloat16)
+    return torch.randn((wl.batch, wl.heads, wl.n, wl.d), generator=g).to(wl.torch_dtype)
 
 
 def gpu_forward_backward(wl, inp, dout):
@@ -54,10 +54,19 @@ def gpu_forward_backward(wl, inp, dout):
     return o.cpu(), lse.cpu(), [None if t is None else t.cpu() for t in grads]
 
 
-def slice_bounds(q, k, v, qg, kg, vg, do, og, window, dilation, causal, gl, row_block=1024):
+def slice_bounds(q, k, v, qg, kg, vg, do, og, window, dilation, causal, gl, row_block=1024,
+                 rnd=ROUND, serr=0.0):
     """The sums of term magnitudes above for one (batch, head): [n, d]
     float64 arrays in, (bq, bk, bv, bqg, bkg, bvg) out (the last three None
-    without global tokens); the final-rounding term is added by the caller."""
+    without global tokens); the final-rounding term is added by the caller.
+
+    ``serr`` > 0 adds the rounding of the fp32 dot products themselves, which
+    the bf16 path's 2^-8 terms dwarf but the fp32 path does not: a score
+    q.k summed in fp32 is off by up to serr * sum_d |q_d k_d|, so P_ij is off
+    by P_ij (s * that + serr) (the exponential and the LSE add about one
+    more unit), and dP_ij = dO_i.v_j by serr * sum_d |dO_d v_d|; then
+    |d dS_ij| <= (dP error) P_ij + (P error) |dP_ij - D_i|,
+    and these enter dq, dk as |dS| does and dv through P."""
     from oracle import allowed_mask
     n, d = q.shape
     s = 1.0 / np.sqrt(d)
@@ -85,18 +94,28 @@ def slice_bounds(q, k, v, qg, kg, vg, do, og, window, dilation, causal, gl, row_
             dD = np.abs(((og[r] - O) * do[r]).sum(axis=1)) + \
                 2.0 ** -22 * (np.abs(og[r]) * np.abs(do[r])).sum(axis=1)
             aK, aQ, adO = np.abs(K), np.abs(Q[r]), np.abs(do[r])
-            BQ[r] = s * (ROUND * (adS @ aK) + dD[:, None] * (P @ aK))
-            BK += s * (ROUND * (adS.T @ aQ) + (P * dD[:, None]).T @ aQ)
-            BV += ROUND * (P.T @ adO)
+            BQ[r] = s * (rnd * (adS @ aK) + dD[:, None] * (P @ aK))
+            BK += s * (rnd * (adS.T @ aQ) + (P * dD[:, None]).T @ aQ)
+            BV += rnd * (P.T @ adO)
+            if serr:
+                dPr = P * (s * serr * (aQ @ aK.T) + serr)       # |error of P|
+                edS = dPr * np.abs(dP - D[:, None]) + P * serr * (adO @ np.abs(V).T)
+                BQ[r] += s * (edS @ aK)
+                BK += s * (edS.T @ aQ)
+                BV += dPr.T @ adO
     return tuple(out) + tuple(outg)
 
 
-def check_grads(wl, inp, dout, o_gpu, got, refs, bh=None, label="", rel=1e-2):
+def check_grads(wl, inp, dout, o_gpu, got, refs, bh=None, label="", rel=1e-2, rnd=ROUND,
+                serr=0.0):
     """Every gradient element within SAFETY * (its bound + the final
     rounding of the reference) + FLOOR; with ``rel``, also the relative RMS
     of each tensor (a global sanity check for inputs without cancellation).
     ``bh`` restricts the check to (batch, head) slices; ``refs`` then holds
-    one tuple of six slice gradients per slice, else the six full tensors."""
+    one tuple of six slice gradients per slice, else the six full tensors.
+    ``rnd`` is the relative rounding of the path's arithmetic (2^-8 for the
+    bf16 path; for fp32, a few units of 2^-24 per sum); ``serr`` that of the
+    fp32 dot products (see slice_bounds)."""
     f = lambda t: None if t is None else t.double().numpy()
     t = {k: f(inp[k]) for k in ("q", "k", "v", "qg", "kg", "vg")}
     do, og = f(dout), f(o_gpu)
@@ -107,7 +126,7 @@ def check_grads(wl, inp, dout, o_gpu, got, refs, bh=None, label="", rel=1e-2):
         sl = lambda x: None if x is None else x[b, h]
         bounds = slice_bounds(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["qg"]), sl(t["kg"]),
                               sl(t["vg"]), do[b, h], og[b, h], wl.window[h], wl.dilation[h],
-                              wl.causal, list(gls[b]))
+                              wl.causal, list(gls[b]), rnd=rnd, serr=serr)
         for gi, name in enumerate(GRADS):
             r = refs[idx][gi] if bh is not None else refs[gi]
             if r is None:
@@ -118,7 +137,7 @@ def check_grads(wl, inp, dout, o_gpu, got, refs, bh=None, label="", rel=1e-2):
             assert np.isfinite(g).all(), f"{label}[{b},{h}]: non-finite {name}"
             # an item without global tokens has no terms in its global gradients
             terms = bounds[gi] if bounds[gi] is not None else 0.0
-            bnd = SAFETY * (terms + ROUND * np.abs(rr)) + FLOOR
+            bnd = SAFETY * (terms + rnd * np.abs(rr)) + FLOOR
             err = np.abs(g - rr)
             ratio = float((err / bnd).max())
             worst = max(worst, ratio)

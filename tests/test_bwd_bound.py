@@ -8,6 +8,8 @@
    twice when it also lies in a row's band (the mistake the "dedup" inputs
    were made to expose; Longformer summary page, section 3-1 "Global
    Attention": every key once) leave it.
+3. Its fp32 form (rounding 2^-20 per sum, plus the fp32 score and dP dot
+   products) covers gradients computed entirely in float32.
 """
 import numpy as np
 import pytest
@@ -128,3 +130,57 @@ def test_bound_catches_a_double_counted_global_key():
             bnd = SAFETY * (bounds[gi] + ROUND * np.abs(r)) + FLOOR
             caught += int((np.abs(wrong[gi] - r) > bnd).any())
     assert caught >= 2
+
+
+def _f32_grads(t, do, og, wl, h, gl):
+    """Every gradient of one head computed in float32 from the float32 O."""
+    f = np.float32
+    n, d = t["q"].shape[2:]
+    s = f(1.0 / np.sqrt(d))
+    rows = np.arange(n)
+    mask = allowed_mask(rows, n, wl.window[h], wl.dilation[h], wl.causal, gl)
+    isg = np.zeros(n, dtype=bool)
+    isg[list(gl)] = True
+    out = [np.zeros((n, d), dtype=f) for _ in range(6)]
+    for sel, names, base in ((~isg, ("q", "k", "v"), 0), (isg, ("qg", "kg", "vg"), 3)):
+        Q, K, V = (t[x][0, h][sel if x[0] == "q" else slice(None)].astype(f) for x in names)
+        dO, O = do[0, h][sel].astype(f), og[0, h][sel].astype(f)
+        S = np.where(mask[sel], s * (Q @ K.T), f(-np.inf)).astype(f)
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m).astype(f)
+        P = (P / P.sum(axis=1, keepdims=True)).astype(f)
+        dP = (dO @ V.T).astype(f)
+        D = (dO * O).sum(axis=1, dtype=f)
+        dS = (P * (dP - D[:, None])).astype(f)
+        out[base][sel] = s * (dS @ K)
+        out[base + 1] += s * (dS.T @ Q)
+        out[base + 2] += P.T @ dO
+    return [x.astype(np.float64) for x in out]
+
+
+@pytest.mark.parametrize("kind", ["normal", "sharp", "dedup"])
+def test_fp32_bound_covers_float32_gradients(kind):
+    inp = make_inputs(WL, 1, kind)
+    dout = cotangent(WL, 1)
+    t = {x: to64(inp[x]) for x in ("q", "k", "v", "qg", "kg", "vg")}
+    do = to64(dout)
+    o, _ = attention(t["q"], t["k"], t["v"], t["qg"], t["kg"], t["vg"], window=list(WL.window),
+                     dilation=list(WL.dilation), causal=WL.causal, global_idx=list(WL.global_idx))
+    og = o.astype(np.float32).astype(np.float64)
+    refs = attention_backward(t["q"], t["k"], t["v"], t["qg"], t["kg"], t["vg"], do,
+                              window=list(WL.window), dilation=list(WL.dilation),
+                              causal=WL.causal, global_idx=list(WL.global_idx))
+    gl = list(WL.global_idx)
+    worst = 0.0
+    for h in range(WL.heads):
+        bounds = slice_bounds(*(t[x][0, h] for x in ("q", "k", "v", "qg", "kg", "vg")), do[0, h],
+                              og[0, h], WL.window[h], WL.dilation[h], WL.causal, gl,
+                              rnd=2.0 ** -20, serr=2.0 ** -21)
+        got = _f32_grads(t, do, og, WL, h, gl)
+        for gi, name in enumerate(GRADS):
+            r = refs[gi][0, h]
+            bnd = SAFETY * (bounds[gi] + 2.0 ** -20 * np.abs(r)) + FLOOR
+            ratio = float((np.abs(got[gi] - r) / bnd).max())
+            worst = max(worst, ratio)
+            assert ratio <= 1.0, f"head {h} {name}: float32 error beyond the fp32 bound ({ratio:.3f})"
+    assert worst > 0.01

@@ -122,10 +122,41 @@ def test_backward_full_size_slices(name, bh, kind):
                 rel=None if kind == "dedup" else 1e-2)
 
 
-def test_backward_rejects_fp32_plans():
-    from sliding_window_attention_banded_amd import Plan, SwattnError
-    x = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
-    lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
-    with Plan(1, 1, 64, 64, 8, 1, False, (), torch.float32) as pl:
-        with pytest.raises(SwattnError):
-            pl.backward(x, x, x, x, lse, x)
+def F(name, B, H, n, window, dilation, causal=False, G=()):
+    win = (window,) * H if isinstance(window, int) else tuple(window)
+    dil = (dilation,) * H if isinstance(dilation, int) else tuple(dilation)
+    return Workload(name, B, H, n, 64, win, dil, causal, tuple(G), "fp32", 0.125)
+
+
+# the fp32 path: the single-head fp32 shape of the benchmark configurations
+# (n 512, window 64) and the same kinds of configuration as above
+SMALL_F32 = [
+    F("f_single_head", 1, 1, 512, 64, 1),
+    F("f_mix_causal", 1, 3, 300, (32, 64, 2), (1, 2, 3), True),
+    F("f_g", 2, 2, 257, (64, 16), (1, 3), False, (0, 100, 256)),
+    F("f_g1_causal", 1, 2, 200, (32, 8), (2, 1), True, (120,)),
+    F("f_per_item", 3, 2, 150, (16, 64), (1, 2), False, ((0, 5), (), (149,))),
+    F("f_wide", 1, 2, 100, (400, 0), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL_F32, ids=lambda w: w.name)
+@pytest.mark.parametrize("kind", ["normal", "sharp", "dedup"])
+def test_backward_fp32(wl, kind):
+    """fp32 gradients against the float64 oracle: the per-element bound with
+    the rounding of fp32 sums (2^-20: a few units of 2^-24 over sums of up
+    to a few thousand terms) in place of the bf16 operands' 2^-8, plus the
+    rounding of the fp32 score and dP dot products (2^-21 = 8 units of 2^-24
+    of sum_d |q_d k_d|: the six-level lane sum, the multiply, the
+    exponential; tests/_bwd.py)."""
+    if kind == "dedup" and not any(len(g) for g in item_globals(wl)):
+        pytest.skip("dedup inputs need global tokens")
+    print(f"[bwd-f32] {wl.name} B{wl.batch} H{wl.heads} n{wl.n} causal={wl.causal} kind={kind}",
+          flush=True)
+    inp = make_inputs(wl, 0, kind)
+    dout = cotangent(wl, 0)
+    o, _, got = gpu_forward_backward(wl, inp, dout)
+    assert all(g is None or g.dtype == torch.float32 for g in got)
+    ref = _oracle_grads(wl, inp, dout)
+    check_grads(wl, inp, dout, o, got, ref, label=f"{wl.name}/{kind}",
+                rel=None if kind == "dedup" else 1e-5, rnd=2.0 ** -20, serr=2.0 ** -21)
