@@ -119,6 +119,7 @@ struct GlobalParams {
   int ksplit;   // keys per split, multiple of 64
   int nqb;      // ceil(ng / 32): blocks of 32 global rows
   int ngroup;   // ceil(nqb / 4): groups of 4 such blocks (one per wave)
+  int stream;   // 1: global_row_stream blocks (bf16, at most one global token per item)
   float c2;
   float scale;
 };
@@ -1128,6 +1129,148 @@ DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char*
 }
 
 // ----------------------------------------------------------------------------
+// Global row by streaming, for bf16 plans with at most one global token per
+// batch item (a classification token): the row's keys are cut into chunks
+// and block (bh, split) streams one chunk of Kg, Vg straight into registers.
+// Two lanes hold a key (lane & 1 holds features 32 (lane & 1) .. +31): the
+// score is sixteen fp32 dot products of bf16 pairs plus the other lane's
+// half; each lane runs its own online softmax over its keys (the lazily
+// raised reference max of the band path) and accumulates P V for its 32
+// features in fp32. The matrix cores would compute 32 rows for the one that
+// exists; what bounds this work is the stream of Kg and Vg, of which each
+// wave keeps two 32-key batches in flight. The block then folds its lanes'
+// partial sums through LDS into one (o, m, l) record per chunk, the record
+// global_block writes.
+template <class T>
+DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, char* st2) {
+  if constexpr (sizeof(T) != 2) {
+    return;  // the host streams bf16 plans only
+  } else {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) char lds_char;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sp = gb % p.nsplit, bh = gb / p.nsplit;
+    const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+    if (gs.n == 0) return;  // workgroup-uniform: no global row in this item
+    const int pos = gs.idx[0];
+    const int k_lo = sp * p.ksplit;
+    int k_hi = min(p.n, k_lo + p.ksplit);
+    if (p.causal) k_hi = min(k_hi, pos + 1);
+    const int nit = k_hi > k_lo ? (k_hi - k_lo + 4 * 32 - 1) / (4 * 32) : 0;  // 128 keys per round
+    const long base = (long)bh * p.n * 128;
+    const int hf = lane & 1, kl = lane >> 1;
+    const char* kb = reinterpret_cast<const char*>(p.kg) + base + hf * 64;
+    const char* vb = reinterpret_cast<const char*>(p.vg) + base + hf * 64;
+
+    // round it, wave w: keys k_lo + 32 (4 it + w) + kl (clamped for the loads)
+    auto fetch = [&](int it, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
+      const int j = min(k_lo + 32 * (4 * it + wave) + kl, k_hi - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kk[c] = *reinterpret_cast<const u32x4*>(kb + (long)j * 128 + 16 * c);
+        vv[c] = *reinterpret_cast<const u32x4*>(vb + (long)j * 128 + 16 * c);
+      }
+    };
+    u32x4 ka[4], va[4], kn[4], vn[4];
+    if (nit > 0) fetch(0, ka, va);
+    if (nit > 1) fetch(1, kn, vn);
+    u32x4 q[4];
+    const char* qrow = reinterpret_cast<const char*>(p.qg) + base + (long)pos * 128 + hf * 64;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+
+    float o[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) o[i] = 0.f;
+    float m = -__builtin_inff(), thr = -__builtin_inff(), moff = 0.f, l = 0.f;
+    auto bf2 = [](unsigned u) { return __builtin_bit_cast(bf16x2, u); };
+    auto step = [&](int it, const u32x4 (&kk)[4], const u32x4 (&vv)[4]) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_fdot2_f32_bf16(bf2(q[c][e]), bf2(kk[c][e]), s, false);
+      s += __shfl_xor(s, 1);
+      if (k_lo + 32 * (4 * it + wave) + kl >= k_hi) s = -__builtin_inff();
+      if (s > thr) {  // the same decision on both lanes of a key
+        const float f = __builtin_amdgcn_exp2f((m - s) * p.c2);  // 0 while m = -inf
+#pragma unroll
+        for (int i = 0; i < 32; ++i) o[i] *= f;
+        l *= f;
+        m = s;
+        thr = s + RESCALE_LOG2 / p.c2;
+        moff = -s * p.c2;
+      }
+      const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s, p.c2, moff));  // 0 for s = -inf
+      l += w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned u = vv[c][e];
+          o[8 * c + 2 * e] = __builtin_fmaf(w, __builtin_bit_cast(float, u << 16), o[8 * c + 2 * e]);
+          o[8 * c + 2 * e + 1] = __builtin_fmaf(w, __builtin_bit_cast(float, u & 0xffff0000u), o[8 * c + 2 * e + 1]);
+        }
+    };
+    for (int it = 0; it < nit; it += 2) {
+      step(it, ka, va);
+      if (it + 2 < nit) fetch(it + 2, ka, va);
+      if (it + 1 < nit) {
+        step(it + 1, kn, vn);
+        if (it + 3 < nit) fetch(it + 3, kn, vn);
+      }
+    }
+
+    // fold: block max, each lane's sums scaled to it, then summed over the
+    // 32 keys of a wave (LDS rows of 64 features, 16-byte chunks swizzled by
+    // the key) and over the four waves
+    typedef __attribute__((address_space(3))) float lds_float;
+    lds_float* sm = (lds_float*)(lds_char*)st2;  // [4] maxima, [4] sums, then [4][64] wave sums
+    float wm = m;
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) wm = fmaxf(wm, __shfl_xor(wm, x));
+    if (lane == 0) sm[wave] = wm;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    const float f = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - M) * p.c2);
+    float lw = l * f;  // the two lanes of a key hold the same l
+#pragma unroll
+    for (int x = 2; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
+    lds_char* wb = (lds_char*)((wave < 2 ? st0 : st1) + (wave & 1) * 8192);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      f32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = o[4 * c + e] * f;
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(wb + kl * 256 + hf * 128 + 16 * (c ^ (kl & 7))) = t;
+    }
+    if (lane == 0) sm[4 + wave] = lw;
+    __syncthreads();
+    {
+      const int d = lane, h2 = d >> 5, c = (d & 31) >> 2;
+      const lds_char* rb = (const lds_char*)((wave < 2 ? st0 : st1) + (wave & 1) * 8192);
+      float acc = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < 32; ++k)
+        acc += *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+            rb + k * 256 + h2 * 128 + 16 * (c ^ (k & 7)) + 4 * (d & 3));
+      sm[8 + 64 * wave + d] = acc;
+    }
+    __syncthreads();
+    if (tid < HD) {
+      const float od = sm[8 + tid] + sm[8 + 64 + tid] + sm[8 + 128 + tid] + sm[8 + 192 + tid];
+      const long slot = ((long)bh * p.ng + 0) * p.nsplit + sp;  // the item's one global row, gi = 0
+      p.part_o[slot * HD + tid] = od;
+      if (tid == 0) {
+        p.part_ml[slot * 2 + 0] = M;
+        p.part_ml[slot * 2 + 1] = sm[4] + sm[5] + sm[6] + sm[7];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // The forward kernel: blocks [0, nband_blocks) are band blocks, the rest
 // global-row blocks. The band blocks come first so that all of them start in
 // the first wave of workgroups; the short global-row blocks fill the
@@ -1147,6 +1290,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd(BandParams bp, GlobalParams g
     const int lb = xcd_remap(b, nband_blocks);
     band_block<T>(bp, lb / bp.parts, lb % bp.parts, st0, st1, st2, gmeta);
   }
+  else if (gp.stream) global_row_stream<T>(gp, b - nband_blocks, st0, st1, st2);
   else global_block<T>(gp, b - nband_blocks, st0, st1, st2);
 }
 

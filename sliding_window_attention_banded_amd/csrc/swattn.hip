@@ -43,6 +43,17 @@ void choose_split(int n, int* nsplit, int* ksplit) {
   *nsplit = (n + ks - 1) / ks;
 }
 
+// Streamed global rows (one global token per item): about eight chunks per
+// row, of 256 to 1024 keys (a multiple of the 128 keys a block takes per
+// round); longer chunks only where 1024-key chunks would exceed MAX_SPLIT.
+void choose_stream_split(int n, int* nsplit, int* ksplit) {
+  int ks = ((n + 7) / 8 + 127) / 128 * 128;
+  ks = std::max(256, std::min(1024, ks));
+  while ((n + ks - 1) / ks > MAX_SPLIT) ks += 128;
+  *ksplit = ks;
+  *nsplit = (n + ks - 1) / ks;
+}
+
 }  // namespace
 
 struct swattn_plan {
@@ -50,6 +61,7 @@ struct swattn_plan {
   int nband_blocks;       // band workgroups (explicit tiles, or the uniform decode)
   int uni_half, uni_right, uni_dil, uni_nqb;  // every head alike: no tile list
   int nsplit, ksplit, nqb, ngroup, nglob_blocks;
+  int gstream;            // global rows by global_row_stream (bf16, |G| <= 1 per item)
   int parts;              // key split of the band tiles (1: none)
   float* band_part;       // [B*H*n][parts][68] partials, NULL without a split
   void* dev_mem;          // one allocation, carved below
@@ -102,6 +114,7 @@ struct Schedule {
   int parts = 1;
   int cus = 256;
   int nsplit = 0, ksplit = 0, nqb = 0, ngroup = 0;
+  int stream = 0;  // global rows by global_row_stream
   long nglob_blocks = 0;
 };
 
@@ -230,7 +243,9 @@ int make_schedule(const swattn_params* p, Schedule* sc) {
   sc->nqb = (ng_max + 31) / 32;
   sc->ngroup = (sc->nqb + BAND_WAVES - 1) / BAND_WAVES;
   if (ng_max > 0) {
-    choose_split(p->n, &sc->nsplit, &sc->ksplit);
+    sc->stream = p->dtype == SWATTN_BF16 && ng_max == 1;
+    if (sc->stream) choose_stream_split(p->n, &sc->nsplit, &sc->ksplit);
+    else choose_split(p->n, &sc->nsplit, &sc->ksplit);
     sc->nglob_blocks = (long)sc->nsplit * sc->ngroup * bh;
     if (sc->nglob_blocks + nband_blocks * parts > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
   }
@@ -272,6 +287,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->nsplit = sc.nsplit;
   pl->ksplit = sc.ksplit;
   pl->nglob_blocks = (int)sc.nglob_blocks;
+  pl->gstream = sc.stream;
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
 
@@ -439,6 +455,7 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   gp.goff = pl->goff; gp.H = pl->H;
   gp.ng = pl->ng; gp.n = pl->n; gp.causal = pl->causal;
   gp.nsplit = pl->nsplit; gp.ksplit = pl->ksplit; gp.nqb = pl->nqb; gp.ngroup = pl->ngroup;
+  gp.stream = pl->gstream;
   gp.c2 = scale * LOG2E; gp.scale = scale;
 
   const bool timed = !pl->ev.empty() && pl->ntimed < swattn_plan::kMaxTimed;
@@ -644,6 +661,7 @@ extern "C" int swattn_forward_noalloc(const swattn_params* p, const void* q, con
   pl.uni_dil = sc.dil[0];
   pl.uni_nqb = ((p->n + sc.dil[0] - 1) / sc.dil[0] + BM - 1) / BM;
   pl.nsplit = sc.nsplit; pl.ksplit = sc.ksplit; pl.nqb = sc.nqb; pl.ngroup = sc.ngroup;
+  pl.gstream = sc.stream;
   pl.nglob_blocks = (int)sc.nglob_blocks;
   pl.parts = sc.parts;
   pl.per_item = sc.per_item;
