@@ -254,7 +254,7 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  BandParams bp;  // the tile decode reads only these fields
+  BandParams bp{};  // the tile decode reads only these fields
   bp.tiles = p.tiles; bp.uni_half = p.uni_half; bp.uni_right = p.uni_right;
   bp.uni_dil = p.uni_dil; bp.uni_nqb = p.uni_nqb; bp.n = p.n;
   const TileRec td = decode_tile(bp, tile);
@@ -489,7 +489,7 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
   const int lane = tid & 63, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  BandParams bp;
+  BandParams bp{};
   bp.tiles = p.tiles; bp.uni_half = p.uni_half; bp.uni_right = p.uni_right;
   bp.uni_dil = p.uni_dil; bp.uni_nqb = p.uni_nqb; bp.n = p.n;
   const TileRec td = decode_tile(bp, tile);

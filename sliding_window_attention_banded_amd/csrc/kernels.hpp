@@ -91,6 +91,7 @@ struct BandParams {
   int parts;
   float* part;
   int fair;     // progress-based wave priorities (no global-row blocks in the launch)
+  int gskip;    // 1: leave the rows of G alone (the global-row blocks write them)
   int H;
   int n;
   int causal;
@@ -120,6 +121,8 @@ struct GlobalParams {
   int nqb;      // ceil(ng / 32): blocks of 32 global rows
   int ngroup;   // ceil(nqb / 4): groups of 4 such blocks (one per wave)
   int stream;   // 1: global_row_stream blocks (bf16, at most one global token per item)
+  int fuse;     // with stream: the chunks' last block folds them (no global_rows_merge)
+  int* gcount;  // [B*H] arrival counters for fuse, zero between launches
   float c2;
   float scale;
 };
@@ -505,9 +508,10 @@ DEV void store_o(float* orow, const WaveAcc& acc, float inv, int g) {
 // then each lane reads back one 16-byte chunk of row 8k + lane/8 and stores
 // it. Written this way the rows stream out past L2 instead of being left
 // dirty for the write-back at the kernel's end. Row qw0 + i sits at
-// position r + (qw0 + i) * dil; rows qw0 + i >= nr are skipped.
+// position r + (qw0 + i) * dil; rows qw0 + i >= nr and position `skip` are
+// skipped.
 DEV void store_o_rows(char* slot, char* obase, const f32x16 (&o)[2], float inv, int lane, int qw0,
-                      int nr, int r, int dil) {
+                      int nr, int r, int dil, int skip = -1) {
   typedef __attribute__((address_space(3))) char lds_char;
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   lds_char* s = (lds_char*)slot;
@@ -529,7 +533,7 @@ DEV void store_o_rows(char* slot, char* obase, const f32x16 (&o)[2], float inv, 
     const u32x4 v =
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(s + row * 128 + ((ch ^ (row & 7)) << 4));
     const int qi = qw0 + row;
-    if (qi < nr)
+    if (qi < nr && r + qi * dil != skip)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (long)(r + qi * dil) * 128 + ch * 16));
   }
 }
@@ -903,6 +907,9 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, td.bh / p.H);
   const int* gix = gs.idx;
   const int ngb = part == 0 ? gs.n : 0;  // the global columns go with the first key part
+  // with gskip (at most one global token per item) that token's row is the
+  // global-row blocks' to write
+  const int skip = p.gskip && gs.n > 0 ? gix[0] : -1;
   int gq[4] = {0, 0, 0, 0};
   int gm = 0;
   int gpos1 = 0;  // the global column when it is the only one (bf16)
@@ -1047,9 +1054,9 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
       // the 4 KB at 4096 * wave.
       const int sa = c.nband % 3;
       char* slot = (sa == 0 ? st0 : (sa == 1 ? st1 : st2)) + 4096 * wave;
-      store_o_rows(slot, reinterpret_cast<char*>(p.o) + base, acc.o, 1.0f / ltot, lane, qw0, nr, r, dil);
-      if (row_ok && p.lse && g == 0) p.lse[(long)bh * p.n + pos_q] = acc.m * p.scale + __logf(ltot);
-    } else if (row_ok) {
+      store_o_rows(slot, reinterpret_cast<char*>(p.o) + base, acc.o, 1.0f / ltot, lane, qw0, nr, r, dil, skip);
+      if (row_ok && pos_q != skip && p.lse && g == 0) p.lse[(long)bh * p.n + pos_q] = acc.m * p.scale + __logf(ltot);
+    } else if (row_ok && pos_q != skip) {
       const float inv = 1.0f / ltot;
       T* orow = reinterpret_cast<T*>(reinterpret_cast<char*>(p.o) + base + (long)pos_q * ROWB);
       store_o(orow, acc, inv, g);
@@ -1128,6 +1135,17 @@ DEV void global_block(const GlobalParams& p, int gb, char* st0, char* st1, char*
   }
 }
 
+// Fold a partial (m, l, a) of one output column into a running (M, L, A):
+// maxima in raw score units, weights exp2((score - max) * c2).
+DEV void lse_fold(float& M, float& L, float& A, float m, float l, float a, float c2) {
+  const float mn = fmaxf(M, m);
+  const float fo = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((M - mn) * c2);
+  const float fn = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+  L = L * fo + l * fn;
+  A = A * fo + a * fn;
+  M = mn;
+}
+
 // ----------------------------------------------------------------------------
 // Global row by streaming, for bf16 plans with at most one global token per
 // batch item (a classification token): the row's keys are cut into chunks
@@ -1151,21 +1169,18 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sp = gb % p.nsplit, bh = gb / p.nsplit;
-    const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
-    if (gs.n == 0) return;  // workgroup-uniform: no global row in this item
-    const int pos = gs.idx[0];
     const int k_lo = sp * p.ksplit;
-    int k_hi = min(p.n, k_lo + p.ksplit);
-    if (p.causal) k_hi = min(k_hi, pos + 1);
-    const int nit = k_hi > k_lo ? (k_hi - k_lo + 4 * 32 - 1) / (4 * 32) : 0;  // 128 keys per round
+    const int k_end = min(p.n, k_lo + p.ksplit);  // the chunk (k_lo < k_end)
     const long base = (long)bh * p.n * 128;
     const int hf = lane & 1, kl = lane >> 1;
     const char* kb = reinterpret_cast<const char*>(p.kg) + base + hf * 64;
     const char* vb = reinterpret_cast<const char*>(p.vg) + base + hf * 64;
 
-    // round it, wave w: keys k_lo + 32 (4 it + w) + kl (clamped for the loads)
+    // round it, wave w: keys k_lo + 32 (4 it + w) + kl (clamped to the chunk
+    // for the loads, which the first two rounds issue before the global
+    // token's position is known)
     auto fetch = [&](int it, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
-      const int j = min(k_lo + 32 * (4 * it + wave) + kl, k_hi - 1);
+      const int j = min(k_lo + 32 * (4 * it + wave) + kl, k_end - 1);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         kk[c] = *reinterpret_cast<const u32x4*>(kb + (long)j * 128 + 16 * c);
@@ -1173,8 +1188,13 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
       }
     };
     u32x4 ka[4], va[4], kn[4], vn[4];
-    if (nit > 0) fetch(0, ka, va);
-    if (nit > 1) fetch(1, kn, vn);
+    fetch(0, ka, va);
+    if (k_end - k_lo > 4 * 32) fetch(1, kn, vn);
+    const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+    if (gs.n == 0) return;  // workgroup-uniform: no global row in this item
+    const int pos = gs.idx[0];
+    const int k_hi = p.causal ? min(k_end, pos + 1) : k_end;
+    const int nit = k_hi > k_lo ? (k_hi - k_lo + 4 * 32 - 1) / (4 * 32) : 0;  // 128 keys per round
     u32x4 q[4];
     const char* qrow = reinterpret_cast<const char*>(p.qg) + base + (long)pos * 128 + hf * 64;
 #pragma unroll
@@ -1258,15 +1278,53 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
       sm[8 + 64 * wave + d] = acc;
     }
     __syncthreads();
-    if (tid < HD) {
-      const float od = sm[8 + tid] + sm[8 + 64 + tid] + sm[8 + 128 + tid] + sm[8 + 192 + tid];
-      const long slot = ((long)bh * p.ng + 0) * p.nsplit + sp;  // the item's one global row, gi = 0
-      p.part_o[slot * HD + tid] = od;
-      if (tid == 0) {
-        p.part_ml[slot * 2 + 0] = M;
-        p.part_ml[slot * 2 + 1] = sm[4] + sm[5] + sm[6] + sm[7];
-      }
+    if (wave != 0) return;
+    const int d = lane;
+    const float od = sm[8 + d] + sm[8 + 64 + d] + sm[8 + 128 + d] + sm[8 + 192 + d];
+    const float L = sm[4] + sm[5] + sm[6] + sm[7];
+    const long row0 = ((long)bh * p.ng + 0) * p.nsplit;  // the item's one global row, gi = 0
+    if (!p.fuse) {  // global_rows_merge folds the chunks after the kernel
+      p.part_o[(row0 + sp) * HD + d] = od;
+      if (d == 0) *reinterpret_cast<f32x2*>(p.part_ml + (row0 + sp) * 2) = f32x2{M, L};
+      return;
     }
+    // The chunks' last block folds them. The records move only through
+    // device-scope atomic stores and loads, which bypass the XCDs' separate
+    // L2 caches; a block's stores are complete (vmcnt 0) before its arrival
+    // on the (batch, head) counter, and the last arrival (the counter's old
+    // value nsplit - 1) issues its loads after the count has returned, so it
+    // reads every record. No cache-wide write-back or invalidate is needed,
+    // and the band blocks around keep their L2 contents. The last arrival
+    // resets the counter for the next launch; band blocks leave the row alone.
+    __hip_atomic_store(p.part_o + (row0 + sp) * HD + d, od, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(p.part_ml + (row0 + sp) * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.part_ml + (row0 + sp) * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmcnt<0>();
+    int old = 0;
+    if (d == 0) old = __hip_atomic_fetch_add(p.gcount + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0);
+    if (old != p.nsplit - 1) return;  // wave-uniform
+    if (d == 0) __hip_atomic_store(p.gcount + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float FM = -__builtin_inff(), FL = 0.f, FA = 0.f;
+    for (int b0 = 0; b0 < p.nsplit; b0 += 8) {
+      float mm[8], ll[8], oo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const long si = row0 + min(b0 + i, p.nsplit - 1);
+        mm[i] = __hip_atomic_load(p.part_ml + si * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ll[i] = __hip_atomic_load(p.part_ml + si * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        oo[i] = __hip_atomic_load(p.part_o + si * HD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (b0 + i < p.nsplit) lse_fold(FM, FL, FA, mm[i], ll[i], oo[i], p.c2);
+    }
+    // the row attends at least to its own key, so FL > 0
+    T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
+    orow[d] = (T)(FA / FL);
+    if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = FM * p.scale + __logf(FL);
   }
 }
 
@@ -1350,14 +1408,6 @@ constexpr int MAX_SPLIT = 256;
 // column t%64 of chunks t/64, t/64 + 4, ...; it loads them in batches of 8
 // (all loads of a batch in flight at once) and folds them into a running
 // (max, sum, output); the four groups are then folded the same way in LDS.
-DEV void lse_fold(float& M, float& L, float& A, float m, float l, float a, float c2) {
-  const float mn = fmaxf(M, m);
-  const float fo = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((M - mn) * c2);
-  const float fn = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
-  L = L * fo + l * fn;
-  A = A * fo + a * fn;
-  M = mn;
-}
 
 // The partials' pointers and counts come first among the arguments so that
 // they can be preloaded into SGPRs (the build's kernarg-preload count): the

@@ -62,6 +62,8 @@ struct swattn_plan {
   int uni_half, uni_right, uni_dil, uni_nqb;  // every head alike: no tile list
   int nsplit, ksplit, nqb, ngroup, nglob_blocks;
   int gstream;            // global rows by global_row_stream (bf16, |G| <= 1 per item)
+  int gfuse;              // gstream, folded in the kernel (no key split): no global_rows_merge
+  int* gcount;            // [B*H] arrival counters of the fused fold, zero between launches
   int parts;              // key split of the band tiles (1: none)
   float* band_part;       // [B*H*n][parts][68] partials, NULL without a split
   void* dev_mem;          // one allocation, carved below
@@ -115,6 +117,7 @@ struct Schedule {
   int cus = 256;
   int nsplit = 0, ksplit = 0, nqb = 0, ngroup = 0;
   int stream = 0;  // global rows by global_row_stream
+  int fuse = 0;    // stream, folded inside the kernel
   long nglob_blocks = 0;
 };
 
@@ -244,6 +247,9 @@ int make_schedule(const swattn_params* p, Schedule* sc) {
   sc->ngroup = (sc->nqb + BAND_WAVES - 1) / BAND_WAVES;
   if (ng_max > 0) {
     sc->stream = p->dtype == SWATTN_BF16 && ng_max == 1;
+    // without a key split the band blocks leave the global row to the
+    // streaming blocks, whose last one per (batch, head) folds the chunks
+    sc->fuse = sc->stream && parts == 1;
     if (sc->stream) choose_stream_split(p->n, &sc->nsplit, &sc->ksplit);
     else choose_split(p->n, &sc->nsplit, &sc->ksplit);
     sc->nglob_blocks = (long)sc->nsplit * sc->ngroup * bh;
@@ -288,6 +294,7 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->ksplit = sc.ksplit;
   pl->nglob_blocks = (int)sc.nglob_blocks;
   pl->gstream = sc.stream;
+  pl->gfuse = sc.fuse;
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipGetDevice"); }
 
@@ -330,8 +337,9 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   const size_t sz_gkv = al(sizeof(float) * (size_t)bh * pl->nchunk * pl->ng32 * 2 * HD);
   const size_t sz_heads = al(sizeof(HeadGeom) * p->heads);
   const size_t sz_split = al(split_bytes);
+  const size_t sz_cnt = al(sizeof(int) * (sc.fuse ? bh : 1));
   const size_t total = sz_tiles + sz_g + sz_goff + sz_po + sz_pml + 2 * sz_stat + 2 * sz_gstat + sz_gkv + sz_heads +
-                       sz_split;
+                       sz_split + sz_cnt;
   e = hipMalloc(&pl->dev_mem, total);
   if (e != hipSuccess) { delete pl; return hip_fail(e, "hipMalloc(plan)"); }
   char* m = static_cast<char*>(pl->dev_mem);
@@ -346,9 +354,10 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->bwd_gdd = reinterpret_cast<float*>(m); m += sz_gstat;
   pl->bwd_part_gkv = reinterpret_cast<float*>(m); m += sz_gkv;
   pl->bwd_heads = reinterpret_cast<HeadGeom*>(m); m += sz_heads;
-  pl->band_part = sz_split ? reinterpret_cast<float*>(m) : nullptr;
-  e = hipSuccess;
-  if (!tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
+  pl->band_part = sz_split ? reinterpret_cast<float*>(m) : nullptr; m += sz_split;
+  pl->gcount = reinterpret_cast<int*>(m);
+  e = hipMemset(pl->gcount, 0, sz_cnt);
+  if (e == hipSuccess && !tiles.empty()) e = hipMemcpy(pl->tiles, tiles.data(), sizeof(TileRec) * tiles.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && !G.empty()) e = hipMemcpy(pl->gidx, G.data(), sizeof(int) * G.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && pl->goff) e = hipMemcpy(pl->goff, goff.data(), sizeof(int) * goff.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess && bwd_g) {
@@ -402,7 +411,7 @@ extern "C" int swattn_kernel_times(swattn_plan* pl, float* band_ms, float* globa
     float a = 0, b = 0;
     hipError_t e = hipEventSynchronize(pl->ev[4 * i + 1]);
     if (e == hipSuccess) e = hipEventElapsedTime(&a, pl->ev[4 * i + 0], pl->ev[4 * i + 1]);
-    if (e == hipSuccess && (pl->ng > 0 || pl->parts > 1)) {
+    if (e == hipSuccess && (pl->parts > 1 || (pl->ng > 0 && !pl->gfuse))) {
       e = hipEventSynchronize(pl->ev[4 * i + 3]);
       if (e == hipSuccess) e = hipEventElapsedTime(&b, pl->ev[4 * i + 2], pl->ev[4 * i + 3]);
     }
@@ -440,7 +449,7 @@ template <class T>
 int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const void* qg,
            const void* kg, const void* vg, void* o, float* lse, hipStream_t st) {
   const float scale = 0.125f;  // 1/sqrt(64)
-  BandParams bp;
+  BandParams bp{};
   bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.lse = lse;
   bp.tiles = pl->tiles; bp.gidx = pl->gidx; bp.goff = pl->goff; bp.ng = pl->ng;
   bp.uni_half = pl->uni_half; bp.uni_right = pl->uni_right; bp.uni_dil = pl->uni_dil;
@@ -449,13 +458,16 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   bp.fair = pl->ng == 0 ? 1 : 0;
   bp.H = pl->H; bp.n = pl->n; bp.causal = pl->causal;
   bp.c2 = scale * LOG2E; bp.scale = scale;
-  GlobalParams gp;
+  GlobalParams gp{};
   gp.qg = qg; gp.kg = kg; gp.vg = vg; gp.o = o; gp.lse = lse; gp.gidx = pl->gidx;
   gp.part_o = pl->part_o; gp.part_ml = pl->part_ml;
   gp.goff = pl->goff; gp.H = pl->H;
   gp.ng = pl->ng; gp.n = pl->n; gp.causal = pl->causal;
   gp.nsplit = pl->nsplit; gp.ksplit = pl->ksplit; gp.nqb = pl->nqb; gp.ngroup = pl->ngroup;
   gp.stream = pl->gstream;
+  gp.fuse = pl->gfuse;
+  gp.gcount = pl->gcount;
+  bp.gskip = pl->gfuse;
   gp.c2 = scale * LOG2E; gp.scale = scale;
 
   const bool timed = !pl->ev.empty() && pl->ntimed < swattn_plan::kMaxTimed;
@@ -478,7 +490,8 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   if (e != hipSuccess) return hip_fail(e, "launch attn_fwd");
   if (timed) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (timed && (pl->parts > 1 || pl->ng > 0)) e = hipEventRecord(ev[2], st);
+  const bool merges = pl->parts > 1 || (pl->ng > 0 && !pl->gfuse);
+  if (timed && merges) e = hipEventRecord(ev[2], st);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (pl->parts > 1) {
     // every row of O and LSE from its key parts (the rows of G are
@@ -489,14 +502,14 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch band_merge");
   }
-  if (pl->ng > 0) {
+  if (pl->ng > 0 && !pl->gfuse) {
     const dim3 mgrid(pl->ng * pl->B * pl->H);
     hipLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, (const float*)gp.part_ml,
                        (const float*)gp.part_o, gp.ng, gp.nsplit, gp);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch global_rows_merge");
   }
-  if (timed && (pl->parts > 1 || pl->ng > 0)) e = hipEventRecord(ev[3], st);
+  if (timed && merges) e = hipEventRecord(ev[3], st);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   return SWATTN_OK;
 }
@@ -624,7 +637,8 @@ extern "C" int swattn_forward_noalloc(const swattn_params* p, const void* q, con
   const size_t o_tiles = 0;
   const size_t o_g = o_tiles + al(sizeof(TileRec) * sc.tiles.size());
   const size_t o_goff = o_g + al(sizeof(int) * sc.G.size());
-  const size_t o_po = o_goff + al(sizeof(int) * sc.goff.size());
+  const size_t o_cnt = o_goff + al(sizeof(int) * sc.goff.size());  // uploaded as zeros on every call
+  const size_t o_po = o_cnt + al(sizeof(int) * (sc.fuse ? bh : 1));
   const size_t nslot = (size_t)bh * sc.ng_max * sc.nsplit;
   const size_t o_pml = o_po + al(sizeof(float) * HD * nslot);
   const size_t o_part = o_pml + al(sizeof(float) * 2 * nslot);
@@ -662,6 +676,7 @@ extern "C" int swattn_forward_noalloc(const swattn_params* p, const void* q, con
   pl.uni_nqb = ((p->n + sc.dil[0] - 1) / sc.dil[0] + BM - 1) / BM;
   pl.nsplit = sc.nsplit; pl.ksplit = sc.ksplit; pl.nqb = sc.nqb; pl.ngroup = sc.ngroup;
   pl.gstream = sc.stream;
+  pl.gfuse = sc.fuse;
   pl.nglob_blocks = (int)sc.nglob_blocks;
   pl.parts = sc.parts;
   pl.per_item = sc.per_item;
@@ -671,6 +686,7 @@ extern "C" int swattn_forward_noalloc(const swattn_params* p, const void* q, con
   pl.part_o = reinterpret_cast<float*>(base + o_po);
   pl.part_ml = reinterpret_cast<float*>(base + o_pml);
   pl.band_part = sc.parts > 1 ? reinterpret_cast<float*>(base + o_part) : nullptr;
+  pl.gcount = reinterpret_cast<int*>(base + o_cnt);
   if (p->dtype == SWATTN_BF16) return launch<__bf16>(&pl, q, k, v, qg, kg, vg, o, lse, st);
   return launch<float>(&pl, q, k, v, qg, kg, vg, o, lse, st);
 }
