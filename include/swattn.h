@@ -115,8 +115,11 @@ int swattn_create(const swattn_params* p, swattn_plan** out);
  *   lse         device fp32 [B, H, n] or NULL to skip.
  * All device pointers must be 16-byte aligned (else ALIGNMENT) and stay
  * valid until the stream reaches the enqueued work. The caller owns every
- * buffer; forward allocates nothing. The current HIP device must be the
- * plan's. Errors: INVALID_ARG (null plan or tensor, NULL-ness of qg/kg/vg
+ * buffer; forward allocates nothing. Forwards on one plan share its
+ * workspace (the global rows' partial records and, with one global token
+ * per item, their arrival counters), so they must not run concurrently:
+ * enqueue them on one stream, or synchronise between them. The current HIP
+ * device must be the plan's. Errors: INVALID_ARG (null plan or tensor, NULL-ness of qg/kg/vg
  * not matching n_global, o overlapping an input, another current device),
  * ALIGNMENT, HIP (launch failure; see swattn_last_error()).
  */
@@ -222,8 +225,10 @@ int swattn_destroy(swattn_plan* plan);
  * forward records HIP events on its stream around its kernels, in two
  * phases: the forward kernel (band rows, global columns and the global rows'
  * partials), and the merges after it (the key-part merge with a key split,
- * the global-row merge with global tokens; from before the first one to
- * after the last one, 0 when there are none). An interval covers the
+ * the global-row merge with global tokens unless the kernel folds the
+ * global row itself, as it does in bf16 with at most one global token per
+ * item and no key split; from before the first one to after the last one,
+ * 0 when there are none). An interval covers the
  * kernels' dispatch and completion, including the cache write-back at a
  * kernel's end; up to 4096 forwards are kept.
  * swattn_kernel_times() waits for the recorded events, returns the average

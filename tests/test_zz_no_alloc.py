@@ -71,6 +71,27 @@ def test_two_calls_match_the_plan_forward():
         compare(wl, o, lse, ref_o, ref_l, label=wl.name)
 
 
+# One global token per item and no key split: the global row is streamed in
+# chunks whose last block folds them, counting arrivals per (batch, head) in
+# the array; the counters must start every call at zero. Two calls in a row,
+# the second smaller, each bit-identical to the plan's forward.
+ONE_G = (Workload("noalloc_one_global", 2, 2, 2000, 64, (128, 128), (1, 1), False, (17,)),
+         Workload("noalloc_one_global_small", 1, 2, 900, 64, (64, 64), (1, 1), True, ((600,),)))
+
+
+def test_one_global_token_folded_in_the_kernel():
+    for wl, seed in ((ONE_G[0], 2), (ONE_G[1], 3)):
+        print(f"[noalloc] {wl.name}: B{wl.batch} H{wl.heads} n{wl.n}", flush=True)
+        inp = make_inputs(wl, seed, "normal")
+        d = _dev(inp)
+        o_ref, l_ref = _plan_forward(wl, d)
+        o, lse = _noalloc_forward(wl, d)
+        assert torch.equal(o, o_ref), f"{wl.name}: O differs from the plan-based forward"
+        assert torch.equal(lse, l_ref), f"{wl.name}: LSE differs from the plan-based forward"
+        ref_o, ref_l = oracle_ref(wl, inp)
+        compare(wl, o.cpu(), lse.cpu(), ref_o, ref_l, label=wl.name)
+
+
 def test_a_problem_beyond_the_array_is_rejected():
     # global-row partials alone: 64 heads x 4096 tokens x 4096 chunks of
     # 256 keys... far above the 32 MiB array; rejected before any launch
