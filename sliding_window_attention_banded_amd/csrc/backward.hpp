@@ -79,6 +79,9 @@ struct BwdParams {
   // block counts of bwd_main: band query blocks (nq), band key blocks (nq),
   // dQg blocks, dKg/dVg blocks, global-column blocks
   int nq, n_gq, n_gkv, n_gcol;
+  // 1: one global token per item; the global rows (dQg partials, dKg, dVg)
+  // and the global columns are streamed on the vector ALUs (n_gkv = 0)
+  int gstream;
   float c2;           // scale * log2(e)
   float scale;
 };
@@ -843,6 +846,250 @@ DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char*
 }
 
 // ----------------------------------------------------------------------------
+// One global token per item, streamed. The global row and the global column
+// are a single row against all n positions: the matrix cores would compute
+// 32 rows for the one that exists, so these blocks stream the n positions
+// through registers instead, two lanes per position (lane & 1 holds the
+// features 32 (lane & 1) .. +31), with fp32 dot products of bf16 pairs and
+// fp32 sums, each wave keeping two 32-position batches in flight. Position
+// batch it of wave w: positions p0 + 32 (4 it + w) + (lane >> 1).
+
+typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
+
+// 32 features of one row (this lane's half) as 16 bf16 pairs
+DEV void load_half(u32x4s (&x)[4], const char* row, int hf) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const u32x4s*>(row + hf * 64 + 16 * c);
+}
+// the full 64-feature dot product of two rows held as halves by lane pairs
+DEV float dot_pairs(const u32x4s (&a)[4], const u32x4s (&b)[4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // the elements go through values: a bit cast of a vector element
+      // expression itself reads the vector's first element
+      const unsigned ua = a[c][e], ub = b[c][e];
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua), __builtin_bit_cast(bf16x2, ub), s, false);
+    }
+  return s + __shfl_xor(s, 1);
+}
+DEV float bf_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+DEV float bf_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+// acc[i] += f * x[i] over the 32 features of a half row
+DEV void axpy_half(float (&acc)[32], float f, const u32x4s (&x)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[8 * c + 2 * e] = __builtin_fmaf(f, bf_lo(x[c][e]), acc[8 * c + 2 * e]);
+      acc[8 * c + 2 * e + 1] = __builtin_fmaf(f, bf_hi(x[c][e]), acc[8 * c + 2 * e + 1]);
+    }
+}
+// f * x (32 features) rounded to bf16: this lane's half of a row
+DEV void scale_half(u32x4s (&t)[4], float f, const u32x4s (&x)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 h{(__bf16)(f * bf_lo(x[c][e])), (__bf16)(f * bf_hi(x[c][e]))};
+      t[c][e] = __builtin_bit_cast(unsigned, h);
+    }
+}
+// The wave's 32 rows (lane pair kl holding row key0 + kl as two 64-byte
+// halves) staged in the wave's 4 KB of LDS and written out as whole 128-byte
+// rows, eight lanes per row, with non-temporal stores (rows >= kend skipped).
+// The same wave reads what it wrote, so no barrier is needed.
+DEV void store_rows_nt(char* w4k, const u32x4s (&t)[4], int kl, int hf, char* dst, int key0, int kend) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) u32x4s lds_u32x4;
+  lds_char* sb = (lds_char*)w4k;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) *(lds_u32x4*)(sb + kl * 128 + 16 * ((4 * hf + c) ^ (kl & 7))) = t[c];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = 8 * k + (lane >> 3), ch = lane & 7;
+    const u32x4s v = *(lds_u32x4*)(sb + row * 128 + 16 * (ch ^ (row & 7)));
+    if (key0 + row < kend)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4s*>(dst + (long)(key0 + row) * 128 + 16 * ch));
+  }
+}
+// Sum acc (32 features per lane, lanes 2k and 2k+1 holding the two halves of
+// position k) over the block's 128 positions into out[0..63] (t < 64 of the
+// first wave write), through st0/st1 as [wave][32][64] floats with 16-byte
+// chunks swizzled by the position.
+DEV void fold_halves(const float (&acc)[32], char* st0, char* st1, float* out) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane & 1, kl = lane >> 1;
+  lds_char* wb = (lds_char*)((wave < 2 ? st0 : st1) + (wave & 1) * 8192);
+  __syncthreads();  // the buffers are free
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    f32x4 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = acc[4 * c + e];
+    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(wb + kl * 256 + hf * 128 + 16 * (c ^ (kl & 7))) = t;
+  }
+  __syncthreads();
+  // thread t: feature t & 63 over the positions of wave t >> 6
+  const int d = lane, h2 = d >> 5, c = (d & 31) >> 2;
+  float sum = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k)
+    sum += *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+        wb + k * 256 + h2 * 128 + 16 * (c ^ (k & 7)) + 4 * (d & 3));
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(st0);  // [4][64]
+  red[wave * HD + d] = sum;
+  __syncthreads();
+  if (tid < HD) *out = red[tid] + red[HD + tid] + red[2 * HD + tid] + red[3 * HD + tid];
+  __syncthreads();
+}
+
+// The global row of (b, h) against one chunk of keys: dKg and dVg of every
+// key of the chunk (zero where the row does not attend: past it when causal,
+// or everywhere in an item without a global token) and the chunk's dQg
+// partial (unscaled), which bwd_gred sums.
+DEV void bwd_grow_stream(const BwdParams& p, int blk, char* st0, char* st1) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane & 1, kl = lane >> 1;
+  const int sp = blk % p.nsplit, bh = blk / p.nsplit;
+  const int k_lo = sp * p.ksplit, k_end = min(p.n, k_lo + p.ksplit);
+  const long base = (long)bh * p.n * ROWB;
+  const char* kgb = reinterpret_cast<const char*>(p.kg) + base;
+  const char* vgb = reinterpret_cast<const char*>(p.vg) + base;
+  char* dkgb = reinterpret_cast<char*>(p.dkg) + base;
+  char* dvgb = reinterpret_cast<char*>(p.dvg) + base;
+  const int nit = (k_end - k_lo + 127) / 128;
+  auto key = [&](int it) { return k_lo + 32 * (4 * it + wave) + kl; };
+  auto fetch = [&](int it, u32x4s (&kk)[4], u32x4s (&vv)[4]) {
+    const long j = min(key(it), k_end - 1);
+    load_half(kk, kgb + j * ROWB, hf);
+    load_half(vv, vgb + j * ROWB, hf);
+  };
+  u32x4s ka[4], va[4], kn[4], vn[4];
+  fetch(0, ka, va);
+  if (nit > 1) fetch(1, kn, vn);
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  const bool has = gs.n > 0;  // workgroup-uniform
+  const int pos = has ? gs.idx[0] : 0;
+  const int k_att = !has ? k_lo : (p.causal ? min(k_end, pos + 1) : k_end);  // keys < k_att attend
+  u32x4s qg[4], dog[4];
+  float lse2 = __builtin_inff(), dd = 0.f;
+  if (has) {
+    load_half(qg, reinterpret_cast<const char*>(p.qg) + base + (long)pos * ROWB, hf);
+    load_half(dog, reinterpret_cast<const char*>(p.dout) + base + (long)pos * ROWB, hf);
+    lse2 = p.glse2[(long)bh * p.ngp];
+    dd = p.gdd[(long)bh * p.ngp];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { qg[c] = u32x4s{0u, 0u, 0u, 0u}; dog[c] = qg[c]; }
+  }
+  float dq[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dq[i] = 0.f;
+  auto step = [&](int it, const u32x4s (&kk)[4], const u32x4s (&vv)[4]) {
+    const int j = key(it);
+    const float s = dot_pairs(qg, kk);
+    const float dp = dot_pairs(dog, vv);
+    const float pr = j < k_att ? __builtin_amdgcn_exp2f(s * p.c2 - lse2) : 0.f;
+    const float ds = pr * (dp - dd);
+    axpy_half(dq, ds, kk);
+    u32x4s t[4];
+    scale_half(t, ds * p.scale, qg);
+    store_rows_nt(st0 + 4096 * wave, t, kl, hf, dkgb, j - kl, k_end);
+    scale_half(t, pr, dog);
+    store_rows_nt(st0 + 4096 * wave, t, kl, hf, dvgb, j - kl, k_end);
+  };
+  for (int it = 0; it < nit; it += 2) {
+    step(it, ka, va);
+    if (it + 2 < nit) fetch(it + 2, ka, va);
+    if (it + 1 < nit) {
+      step(it + 1, kn, vn);
+      if (it + 3 < nit) fetch(it + 3, kn, vn);
+    }
+  }
+  if (!has) return;  // workgroup-uniform: no dQg partial for an item without G
+  float out = 0.f;
+  fold_halves(dq, st0, st1, &out);
+  if (tid < HD) p.part_dqg[(((long)bh * p.ng + 0) * p.nsplit + sp) * HD + tid] = out;
+}
+
+// The global column of (b, h) against one chunk of query rows: the dK[g],
+// dV[g] terms (unscaled dK) of the rows that attend to the global key g
+// from outside their band (rows of G have LSE +inf, so P = 0), one partial
+// per chunk for bwd_gred.
+DEV void bwd_gcol_stream(const BwdParams& p, int blk, char* st0, char* st1) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane & 1, kl = lane >> 1;
+  const int ch = blk % p.nchunk, bh = blk / p.nchunk;
+  const int qbeg = ch * p.gcol_qc, qend = min(p.n, qbeg + p.gcol_qc);
+  const long base = (long)bh * p.n * ROWB;
+  const char* qb = reinterpret_cast<const char*>(p.q) + base;
+  const char* db = reinterpret_cast<const char*>(p.dout) + base;
+  const float* lse2 = p.lse2 + (long)bh * p.n;
+  const float* ddr = p.dd + (long)bh * p.n;
+  const int nit = (qend - qbeg + 127) / 128;
+  auto row = [&](int it) { return qbeg + 32 * (4 * it + wave) + kl; };
+  auto fetch = [&](int it, u32x4s (&qq)[4], u32x4s (&oo)[4], float& l2, float& d) {
+    const long i = min(row(it), qend - 1);
+    load_half(qq, qb + i * ROWB, hf);
+    load_half(oo, db + i * ROWB, hf);
+    l2 = lse2[i];
+    d = ddr[i];
+  };
+  u32x4s qa[4], oa[4], qn[4], on[4];
+  float la, da, ln, dn;
+  fetch(0, qa, oa, la, da);
+  if (nit > 1) fetch(1, qn, on, ln, dn);
+  const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
+  if (gs.n == 0) return;  // workgroup-uniform: no global key in this item
+  const int gpos = gs.idx[0];
+  const HeadGeom hg = p.heads[bh % p.H];
+  u32x4s kg[4], vg[4];
+  load_half(kg, reinterpret_cast<const char*>(p.k) + base + (long)gpos * ROWB, hf);
+  load_half(vg, reinterpret_cast<const char*>(p.v) + base + (long)gpos * ROWB, hf);
+  float dk[32], dv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) { dk[i] = 0.f; dv[i] = 0.f; }
+  auto step = [&](int it, const u32x4s (&qq)[4], const u32x4s (&oo)[4], float l2, float d) {
+    const int i = row(it);
+    const int dl = i - gpos;  // the row holds g in its band iff g is a band key of it
+    const bool inband = dl >= -hg.right * hg.dil && dl <= hg.half * hg.dil && dl % hg.dil == 0;
+    const bool ok = i < qend && !inband && !(p.causal && gpos > i);
+    const float s = dot_pairs(qq, kg);
+    const float dp = dot_pairs(oo, vg);
+    const float pr = ok ? __builtin_amdgcn_exp2f(s * p.c2 - l2) : 0.f;  // l2 = +inf on rows of G
+    const float ds = pr * (dp - d);
+    axpy_half(dk, ds, qq);
+    axpy_half(dv, pr, oo);
+  };
+  for (int it = 0; it < nit; it += 2) {
+    step(it, qa, oa, la, da);
+    if (it + 2 < nit) fetch(it + 2, qa, oa, la, da);
+    if (it + 1 < nit) {
+      step(it + 1, qn, on, ln, dn);
+      if (it + 3 < nit) fetch(it + 3, qn, on, ln, dn);
+    }
+  }
+  float outk = 0.f, outv = 0.f;
+  fold_halves(dk, st0, st1, &outk);
+  fold_halves(dv, st0, st1, &outv);
+  if (tid < HD) {
+    float* rec = p.part_gkv + (((long)bh * p.nchunk + ch) * p.ng32 + 0) * (2 * HD);
+    rec[tid] = outk;
+    rec[HD + tid] = outv;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Reduction for the global tokens, after bwd_main: one block per (b*h, global
 // row). dqg[g] = s * sum of the chunk partials; dk[g], dv[g] gain the
 // global-column terms of every query chunk.
@@ -893,9 +1140,17 @@ __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char st2[QSTAGEB];
   __shared__ int gmeta[2][KT];
   int b = blockIdx.x;
-  if (b < p.n_gcol) { bwd_gcol_block(p, b, st0, st1, st2); return; }
+  if (b < p.n_gcol) {
+    if (p.gstream) bwd_gcol_stream(p, b, st0, st1);
+    else bwd_gcol_block(p, b, st0, st1, st2);
+    return;
+  }
   b -= p.n_gcol;
-  if (b < p.n_gq) { bwd_gq_block(p, b, st0, st1, st2); return; }
+  if (b < p.n_gq) {
+    if (p.gstream) bwd_grow_stream(p, b, st0, st1);
+    else bwd_gq_block(p, b, st0, st1, st2);
+    return;
+  }
   b -= p.n_gq;
   if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, st1, gmeta[0]); return; }
   b -= p.n_gkv;

@@ -63,6 +63,7 @@ struct swattn_plan {
   int nsplit, ksplit, nqb, ngroup, nglob_blocks;
   int gstream;            // global rows by global_row_stream (bf16, |G| <= 1 per item)
   int gfuse;              // gstream, folded in the kernel (no key split): no global_rows_merge
+  int bwd_gstream;        // backward: global row and column streamed (bf16, |G| <= 1 per item)
   int* gcount;            // [B*H] arrival counters of the fused fold, zero between launches
   int parts;              // key split of the band tiles (1: none)
   float* band_part;       // [B*H*n][parts][68] partials, NULL without a split
@@ -323,7 +324,10 @@ extern "C" int swattn_create(const swattn_params* p, swattn_plan** out) {
   pl->n_gq = bwd_g ? (int)((long)pl->bwd_nsplit * pl->ngroup * bh) : 0;
   pl->nkgb = bwd_g ? ((pl->ng + 31) / 32 + BAND_WAVES - 1) / BAND_WAVES : 0;
   {
-    const long n_gkv = bwd_g ? bh * ((p->n + BM * GKV_GROUPS - 1) / (BM * GKV_GROUPS)) : 0;
+    // one global token per item: the global rows and columns are streamed
+    // (bwd_grow_stream writes dKg, dVg with the dQg partials)
+    pl->bwd_gstream = bwd_g && pl->ng == 1;
+    const long n_gkv = bwd_g && !pl->bwd_gstream ? bh * ((p->n + BM * GKV_GROUPS - 1) / (BM * GKV_GROUPS)) : 0;
     const long n_gcol = bwd_g ? bh * (long)pl->nchunk * pl->nkgb : 0;
     const long nbwd = 2 * nband_blocks + (long)pl->n_gq + n_gkv + n_gcol;
     if (nbwd > 0x7fffffffL) {
@@ -740,6 +744,7 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   bp.nq = pl->nband_blocks;
   bp.n_gq = pl->n_gq;
   bp.n_gkv = pl->n_gkv; bp.n_gcol = pl->n_gcol;
+  bp.gstream = pl->bwd_gstream;
   bp.c2 = scale * LOG2E; bp.scale = scale;
   const long rows = (long)pl->B * pl->H * pl->n;
   if (pl->dtype == SWATTN_FP32) {
