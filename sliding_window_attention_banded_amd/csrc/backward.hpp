@@ -80,7 +80,8 @@ struct BwdParams {
   // dQg blocks, dKg/dVg blocks, global-column blocks
   int nq, n_gq, n_gkv, n_gcol;
   // 1: one global token per item; the global rows (dQg partials, dKg, dVg)
-  // and the global columns are streamed on the vector ALUs (n_gkv = 0)
+  // and the global columns are streamed on the vector ALUs (n_gkv = 0),
+  // by the bwd_main<true> instantiation
   int gstream;
   float c2;           // scale * log2(e)
   float scale;
@@ -1134,6 +1135,10 @@ __global__ __launch_bounds__(256) void bwd_gred(BwdParams p) {
 // blocks start at once and the band blocks pack around them (on the encoder
 // workload 117.5 us instead of 133 us with them last).
 
+// Two instantiations: GSTREAM = true for plans with one global token per
+// item (the streamed global row and column), false for every other plan, so
+// that the streaming code does not enlarge the kernel that the others run.
+template <bool GSTREAM>
 __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char st0[QSTAGEB];
   __shared__ __attribute__((aligned(1024))) char st1[QSTAGEB];
@@ -1141,19 +1146,21 @@ __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
   __shared__ int gmeta[2][KT];
   int b = blockIdx.x;
   if (b < p.n_gcol) {
-    if (p.gstream) bwd_gcol_stream(p, b, st0, st1);
+    if constexpr (GSTREAM) bwd_gcol_stream(p, b, st0, st1);
     else bwd_gcol_block(p, b, st0, st1, st2);
     return;
   }
   b -= p.n_gcol;
   if (b < p.n_gq) {
-    if (p.gstream) bwd_grow_stream(p, b, st0, st1);
+    if constexpr (GSTREAM) bwd_grow_stream(p, b, st0, st1);
     else bwd_gq_block(p, b, st0, st1, st2);
     return;
   }
   b -= p.n_gq;
-  if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, st1, gmeta[0]); return; }
-  b -= p.n_gkv;
+  if constexpr (!GSTREAM) {
+    if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, st1, gmeta[0]); return; }
+    b -= p.n_gkv;
+  }
   if (b < p.nq) { bwd_dq_block(p, xcd_remap(b, p.nq), st0, st1, st2, gmeta); return; }
   b -= p.nq;
   bwd_dkv_block(p, xcd_remap(b, p.nq), st0, st1, st2);

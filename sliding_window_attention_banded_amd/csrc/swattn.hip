@@ -763,7 +763,9 @@ extern "C" int swattn_backward(swattn_plan* pl, const void* q, const void* k, co
   hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((rows * 4 + 255) / 256)), dim3(256), 0, st, bp, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch bwd_prep");
-  hipLaunchKernelGGL(bwd_main, dim3(2 * bp.nq + bp.n_gq + bp.n_gkv + bp.n_gcol), dim3(256), 0, st, bp);
+  const dim3 mgrid(2 * bp.nq + bp.n_gq + bp.n_gkv + bp.n_gcol);
+  if (bp.gstream) hipLaunchKernelGGL(bwd_main<true>, mgrid, dim3(256), 0, st, bp);
+  else hipLaunchKernelGGL(bwd_main<false>, mgrid, dim3(256), 0, st, bp);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch bwd_main");
   if (pl->ng > 0) {
