@@ -1334,7 +1334,9 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
 // the first wave of workgroups; the short global-row blocks fill the
 // workgroup slots that band blocks at the sequence ends free early.
 
-template <class T>
+// GSTREAM: the instantiation for plans whose global rows are streamed
+// (global_row_stream); the others leave that code out of their kernel.
+template <class T, bool GSTREAM>
 __global__ __launch_bounds__(256, 3) void attn_fwd(BandParams bp, GlobalParams gp, int nband_blocks) {
   constexpr int STAGEB = 2 * KT * ElemTraits<T>::ROWB;
   constexpr int NS = RingCfg<T>::NS;
@@ -1348,7 +1350,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd(BandParams bp, GlobalParams g
     const int lb = xcd_remap(b, nband_blocks);
     band_block<T>(bp, lb / bp.parts, lb % bp.parts, st0, st1, st2, gmeta);
   }
-  else if (gp.stream) global_row_stream<T>(gp, b - nband_blocks, st0, st1, st2);
+  else if constexpr (GSTREAM) global_row_stream<T>(gp, b - nband_blocks, st0, st1, st2);
   else global_block<T>(gp, b - nband_blocks, st0, st1, st2);
 }
 

@@ -489,7 +489,12 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
   hipError_t e = hipSuccess;
   if (timed) e = hipEventRecord(ev[0], st);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  hipLaunchKernelGGL(attn_fwd<T>, grid, block, 0, st, bp, gp, nfwd);
+  if constexpr (sizeof(T) == 2) {
+    if (gp.stream) hipLaunchKernelGGL((attn_fwd<T, true>), grid, block, 0, st, bp, gp, nfwd);
+    else hipLaunchKernelGGL((attn_fwd<T, false>), grid, block, 0, st, bp, gp, nfwd);
+  } else {
+    hipLaunchKernelGGL((attn_fwd<T, false>), grid, block, 0, st, bp, gp, nfwd);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch attn_fwd");
   if (timed) e = hipEventRecord(ev[1], st);
