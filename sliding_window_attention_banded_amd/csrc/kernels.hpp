@@ -1146,19 +1146,25 @@ DEV void lse_fold(float& M, float& L, float& A, float m, float l, float a, float
   M = mn;
 }
 
+// Rounds of 16 keys each wave of a streaming global-row block keeps in
+// flight (8 would be a whole 512-key chunk, but spill registers at three
+// waves per SIMD).
+constexpr int GSTREAM_DEPTH = 6;
+
 // ----------------------------------------------------------------------------
 // Global row by streaming, for bf16 plans with at most one global token per
 // batch item (a classification token): the row's keys are cut into chunks
 // and block (bh, split) streams one chunk of Kg, Vg straight into registers.
-// Two lanes hold a key (lane & 1 holds features 32 (lane & 1) .. +31): the
-// score is sixteen fp32 dot products of bf16 pairs plus the other lane's
-// half; each lane runs its own online softmax over its keys (the lazily
-// raised reference max of the band path) and accumulates P V for its 32
+// Four lanes hold a key (lane % 4 holds features 16 (lane % 4) .. +15): the
+// score is eight fp32 dot products of bf16 pairs plus the other lanes'
+// parts; each lane runs its own online softmax over its keys (the lazily
+// raised reference max of the band path) and accumulates P V for its 16
 // features in fp32. The matrix cores would compute 32 rows for the one that
-// exists; what bounds this work is the stream of Kg and Vg, of which each
-// wave keeps two 32-key batches in flight. The block then folds its lanes'
-// partial sums through LDS into one (o, m, l) record per chunk, the record
-// global_block writes.
+// exists; what bounds this work is the stream of Kg and Vg: with 16 features
+// per lane a lane's registers hold GSTREAM_DEPTH rounds of 16 keys per wave,
+// most of a 512-key chunk, in flight at once. The block then folds its
+// lanes' partial sums through LDS into one (o, m, l) record per chunk, the
+// record global_block writes.
 template <class T>
 DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, char* st2) {
   if constexpr (sizeof(T) != 2) {
@@ -1166,57 +1172,66 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
   } else {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) char lds_char;
+    constexpr int LPK = 4;              // lanes per key
+    constexpr int DPL = HD / LPK;       // features per lane
+    constexpr int CH = DPL * 2 / 16;    // 16-byte pieces of a lane's features
+    constexpr int KPW = 64 / LPK;       // keys per wave and round
+    constexpr int DEPTH = GSTREAM_DEPTH;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sp = gb % p.nsplit, bh = gb / p.nsplit;
     const int k_lo = sp * p.ksplit;
     const int k_end = min(p.n, k_lo + p.ksplit);  // the chunk (k_lo < k_end)
     const long base = (long)bh * p.n * 128;
-    const int hf = lane & 1, kl = lane >> 1;
-    const char* kb = reinterpret_cast<const char*>(p.kg) + base + hf * 64;
-    const char* vb = reinterpret_cast<const char*>(p.vg) + base + hf * 64;
+    const int part = lane % LPK, kq = lane / LPK;
+    const char* kb = reinterpret_cast<const char*>(p.kg) + base + part * (2 * DPL);
+    const char* vb = reinterpret_cast<const char*>(p.vg) + base + part * (2 * DPL);
 
-    // round it, wave w: keys k_lo + 32 (4 it + w) + kl (clamped to the chunk
-    // for the loads, which the first two rounds issue before the global
-    // token's position is known)
-    auto fetch = [&](int it, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
-      const int j = min(k_lo + 32 * (4 * it + wave) + kl, k_end - 1);
+    // round it, wave w: keys k_lo + KPW (4 it + w) + kq (clamped to the
+    // chunk for the loads, which the first DEPTH rounds issue before the
+    // global token's position is known)
+    auto key = [&](int it) { return k_lo + KPW * (4 * it + wave) + kq; };
+    auto fetch = [&](int it, u32x4 (&kk)[CH], u32x4 (&vv)[CH]) {
+      const long j = min(key(it), k_end - 1);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        kk[c] = *reinterpret_cast<const u32x4*>(kb + (long)j * 128 + 16 * c);
-        vv[c] = *reinterpret_cast<const u32x4*>(vb + (long)j * 128 + 16 * c);
+      for (int c = 0; c < CH; ++c) {
+        kk[c] = *reinterpret_cast<const u32x4*>(kb + j * 128 + 16 * c);
+        vv[c] = *reinterpret_cast<const u32x4*>(vb + j * 128 + 16 * c);
       }
     };
-    u32x4 ka[4], va[4], kn[4], vn[4];
-    fetch(0, ka, va);
-    if (k_end - k_lo > 4 * 32) fetch(1, kn, vn);
+    const int nit_ld = (k_end - k_lo + 4 * KPW - 1) / (4 * KPW);
+    u32x4 kbuf[DEPTH][CH], vbuf[DEPTH][CH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s)
+      if (s < nit_ld) fetch(s, kbuf[s], vbuf[s]);
     const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
     if (gs.n == 0) return;  // workgroup-uniform: no global row in this item
     const int pos = gs.idx[0];
     const int k_hi = p.causal ? min(k_end, pos + 1) : k_end;
-    const int nit = k_hi > k_lo ? (k_hi - k_lo + 4 * 32 - 1) / (4 * 32) : 0;  // 128 keys per round
-    u32x4 q[4];
-    const char* qrow = reinterpret_cast<const char*>(p.qg) + base + (long)pos * 128 + hf * 64;
+    const int nit = k_hi > k_lo ? (k_hi - k_lo + 4 * KPW - 1) / (4 * KPW) : 0;  // 4 KPW keys per round
+    u32x4 q[CH];
+    const char* qrow = reinterpret_cast<const char*>(p.qg) + base + (long)pos * 128 + part * (2 * DPL);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) q[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+    for (int c = 0; c < CH; ++c) q[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
 
-    float o[32];
+    float o[DPL];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] = 0.f;
+    for (int i = 0; i < DPL; ++i) o[i] = 0.f;
     float m = -__builtin_inff(), thr = -__builtin_inff(), moff = 0.f, l = 0.f;
     auto bf2 = [](unsigned u) { return __builtin_bit_cast(bf16x2, u); };
-    auto step = [&](int it, const u32x4 (&kk)[4], const u32x4 (&vv)[4]) {
+    auto step = [&](int it, const u32x4 (&kk)[CH], const u32x4 (&vv)[CH]) {
       float s = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_fdot2_f32_bf16(bf2(q[c][e]), bf2(kk[c][e]), s, false);
       s += __shfl_xor(s, 1);
-      if (k_lo + 32 * (4 * it + wave) + kl >= k_hi) s = -__builtin_inff();
-      if (s > thr) {  // the same decision on both lanes of a key
+      s += __shfl_xor(s, 2);
+      if (key(it) >= k_hi) s = -__builtin_inff();
+      if (s > thr) {  // the same decision on the lanes of a key
         const float f = __builtin_amdgcn_exp2f((m - s) * p.c2);  // 0 while m = -inf
 #pragma unroll
-        for (int i = 0; i < 32; ++i) o[i] *= f;
+        for (int i = 0; i < DPL; ++i) o[i] *= f;
         l *= f;
         m = s;
         thr = s + RESCALE_LOG2 / p.c2;
@@ -1225,7 +1240,7 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
       const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s, p.c2, moff));  // 0 for s = -inf
       l += w;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const unsigned u = vv[c][e];
@@ -1233,18 +1248,20 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
           o[8 * c + 2 * e + 1] = __builtin_fmaf(w, __builtin_bit_cast(float, u & 0xffff0000u), o[8 * c + 2 * e + 1]);
         }
     };
-    for (int it = 0; it < nit; it += 2) {
-      step(it, ka, va);
-      if (it + 2 < nit) fetch(it + 2, ka, va);
-      if (it + 1 < nit) {
-        step(it + 1, kn, vn);
-        if (it + 3 < nit) fetch(it + 3, kn, vn);
+    for (int it0 = 0; it0 < nit; it0 += DEPTH) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        const int it = it0 + s;
+        if (it < nit) {
+          step(it, kbuf[s], vbuf[s]);
+          if (it + DEPTH < nit) fetch(it + DEPTH, kbuf[s], vbuf[s]);
+        }
       }
     }
 
     // fold: block max, each lane's sums scaled to it, then summed over the
-    // 32 keys of a wave (LDS rows of 64 features, 16-byte chunks swizzled by
-    // the key) and over the four waves
+    // KPW keys of a wave (LDS rows of 64 features, 16-byte chunks swizzled
+    // by the key) and over the four waves
     typedef __attribute__((address_space(3))) float lds_float;
     lds_float* sm = (lds_float*)(lds_char*)st2;  // [4] maxima, [4] sums, then [4][64] wave sums
     float wm = m;
@@ -1254,27 +1271,27 @@ DEV void global_row_stream(const GlobalParams& p, int gb, char* st0, char* st1, 
     __syncthreads();
     const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
     const float f = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - M) * p.c2);
-    float lw = l * f;  // the two lanes of a key hold the same l
+    float lw = l * f;  // the lanes of a key hold the same l
 #pragma unroll
-    for (int x = 2; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
-    lds_char* wb = (lds_char*)((wave < 2 ? st0 : st1) + (wave & 1) * 8192);
+    for (int x = LPK; x < 64; x <<= 1) lw += __shfl_xor(lw, x);
+    lds_char* wb = (lds_char*)(st0 + 4096 * wave);  // [KPW][64] floats
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < DPL / 4; ++c) {
       f32x4 t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[e] = o[4 * c + e] * f;
-      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(wb + kl * 256 + hf * 128 + 16 * (c ^ (kl & 7))) = t;
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(wb + kq * 256 + part * (4 * DPL) +
+                                                                   16 * (c ^ (kq % (DPL / 4)))) = t;
     }
     if (lane == 0) sm[4 + wave] = lw;
     __syncthreads();
     {
-      const int d = lane, h2 = d >> 5, c = (d & 31) >> 2;
-      const lds_char* rb = (const lds_char*)((wave < 2 ? st0 : st1) + (wave & 1) * 8192);
+      const int d = lane, pd = d / DPL, c = (d % DPL) / 4;
       float acc = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < 32; ++k)
+#pragma unroll
+      for (int k = 0; k < KPW; ++k)
         acc += *reinterpret_cast<const __attribute__((address_space(3))) float*>(
-            rb + k * 256 + h2 * 128 + 16 * (c ^ (k & 7)) + 4 * (d & 3));
+            wb + k * 256 + pd * (4 * DPL) + 16 * (c ^ (k % (DPL / 4))) + 4 * (d % 4));
       sm[8 + 64 * wave + d] = acc;
     }
     __syncthreads();
