@@ -850,23 +850,31 @@ DEV void bwd_gcol_block(const BwdParams& p, int blk, char* st0, char* st1, char*
 // One global token per item, streamed. The global row and the global column
 // are a single row against all n positions: the matrix cores would compute
 // 32 rows for the one that exists, so these blocks stream the n positions
-// through registers instead, two lanes per position (lane & 1 holds the
-// features 32 (lane & 1) .. +31), with fp32 dot products of bf16 pairs and
-// fp32 sums, each wave keeping two 32-position batches in flight. Position
-// batch it of wave w: positions p0 + 32 (4 it + w) + (lane >> 1).
+// through registers instead, four lanes per position (lane % 4 holds the
+// features 16 (lane % 4) .. +15), with fp32 dot products of bf16 pairs and
+// fp32 sums; with 16 features per lane the registers hold many positions,
+// and each wave keeps SDEPTH rounds of 16 positions in flight. Round it of
+// wave w: positions p0 + 16 (4 it + w) + (lane / 4).
 
 typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
+constexpr int SLPK = 4;            // lanes per position
+constexpr int SDPL = HD / SLPK;    // features per lane
+constexpr int SCH = SDPL * 2 / 16; // 16-byte pieces of a lane's features
+constexpr int SKPW = 64 / SLPK;    // positions per wave and round
+// rounds in flight per wave (bwd_main runs two waves per SIMD, so the
+// registers are there)
+constexpr int SDEPTH = 8;
 
-// 32 features of one row (this lane's half) as 16 bf16 pairs
-DEV void load_half(u32x4s (&x)[4], const char* row, int hf) {
+// this lane's 16 features of one row, as 8 bf16 pairs
+DEV void load_part(u32x4s (&x)[SCH], const char* row, int part) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const u32x4s*>(row + hf * 64 + 16 * c);
+  for (int c = 0; c < SCH; ++c) x[c] = *reinterpret_cast<const u32x4s*>(row + part * (2 * SDPL) + 16 * c);
 }
-// the full 64-feature dot product of two rows held as halves by lane pairs
-DEV float dot_pairs(const u32x4s (&a)[4], const u32x4s (&b)[4]) {
+// the full 64-feature dot product of two rows held in parts by 4 lanes
+DEV float dot_parts(const u32x4s (&a)[SCH], const u32x4s (&b)[SCH]) {
   float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < SCH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // the elements go through values: a bit cast of a vector element
@@ -874,76 +882,78 @@ DEV float dot_pairs(const u32x4s (&a)[4], const u32x4s (&b)[4]) {
       const unsigned ua = a[c][e], ub = b[c][e];
       s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua), __builtin_bit_cast(bf16x2, ub), s, false);
     }
-  return s + __shfl_xor(s, 1);
+  s += __shfl_xor(s, 1);
+  return s + __shfl_xor(s, 2);
 }
 DEV float bf_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
 DEV float bf_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
-// acc[i] += f * x[i] over the 32 features of a half row
-DEV void axpy_half(float (&acc)[32], float f, const u32x4s (&x)[4]) {
+// acc[i] += f * x[i] over this lane's features
+DEV void axpy_part(float (&acc)[SDPL], float f, const u32x4s (&x)[SCH]) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < SCH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[8 * c + 2 * e] = __builtin_fmaf(f, bf_lo(x[c][e]), acc[8 * c + 2 * e]);
       acc[8 * c + 2 * e + 1] = __builtin_fmaf(f, bf_hi(x[c][e]), acc[8 * c + 2 * e + 1]);
     }
 }
-// f * x (32 features) rounded to bf16: this lane's half of a row
-DEV void scale_half(u32x4s (&t)[4], float f, const u32x4s (&x)[4]) {
+// f * x over this lane's features, rounded to bf16
+DEV void scale_part(u32x4s (&t)[SCH], float f, const u32x4s (&x)[SCH]) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < SCH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bf16x2 h{(__bf16)(f * bf_lo(x[c][e])), (__bf16)(f * bf_hi(x[c][e]))};
       t[c][e] = __builtin_bit_cast(unsigned, h);
     }
 }
-// The wave's 32 rows (lane pair kl holding row key0 + kl as two 64-byte
-// halves) staged in the wave's 4 KB of LDS and written out as whole 128-byte
-// rows, eight lanes per row, with non-temporal stores (rows >= kend skipped).
-// The same wave reads what it wrote, so no barrier is needed.
-DEV void store_rows_nt(char* w4k, const u32x4s (&t)[4], int kl, int hf, char* dst, int key0, int kend) {
+// The wave's 16 rows (the 4 lanes of position kq holding row key0 + kq in
+// 32-byte parts) staged in the wave's 2 KB of LDS and written out as whole
+// 128-byte rows, eight lanes per row, with non-temporal stores (rows >= kend
+// skipped). The same wave reads what it wrote, so no barrier is needed.
+DEV void store_rows_nt(char* w2k, const u32x4s (&t)[SCH], int kq, int part, char* dst, int key0, int kend) {
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) u32x4s lds_u32x4;
-  lds_char* sb = (lds_char*)w4k;
+  lds_char* sb = (lds_char*)w2k;
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) *(lds_u32x4*)(sb + kl * 128 + 16 * ((4 * hf + c) ^ (kl & 7))) = t[c];
+  for (int c = 0; c < SCH; ++c) *(lds_u32x4*)(sb + kq * 128 + 16 * ((SCH * part + c) ^ (kq & 7))) = t[c];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < SKPW / 8; ++k) {
     const int row = 8 * k + (lane >> 3), ch = lane & 7;
     const u32x4s v = *(lds_u32x4*)(sb + row * 128 + 16 * (ch ^ (row & 7)));
     if (key0 + row < kend)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4s*>(dst + (long)(key0 + row) * 128 + 16 * ch));
   }
 }
-// Sum acc (32 features per lane, lanes 2k and 2k+1 holding the two halves of
-// position k) over the block's 128 positions into out[0..63] (t < 64 of the
-// first wave write), through st0/st1 as [wave][32][64] floats with 16-byte
-// chunks swizzled by the position.
-DEV void fold_halves(const float (&acc)[32], char* st0, char* st1, float* out) {
+// Sum acc (this lane's features of position kq) over the block's 4 x SKPW
+// positions into *out (feature t of the first wave, t < 64), through st0 as
+// [wave][SKPW][64] floats with 16-byte chunks swizzled by the position, then
+// [4][64] wave sums.
+DEV void fold_parts(const float (&acc)[SDPL], char* st0, float* out) {
   typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) float lds_float;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hf = lane & 1, kl = lane >> 1;
-  lds_char* wb = (lds_char*)((wave < 2 ? st0 : st1) + (wave & 1) * 8192);
+  const int part = lane % SLPK, kq = lane / SLPK;
+  lds_char* wb = (lds_char*)(st0 + wave * (SKPW * 256));
   __syncthreads();  // the buffers are free
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < SDPL / 4; ++c) {
     f32x4 t;
 #pragma unroll
     for (int e = 0; e < 4; ++e) t[e] = acc[4 * c + e];
-    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(wb + kl * 256 + hf * 128 + 16 * (c ^ (kl & 7))) = t;
+    *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(wb + kq * 256 + part * (4 * SDPL) +
+                                                                 16 * (c ^ (kq % (SDPL / 4)))) = t;
   }
   __syncthreads();
-  // thread t: feature t & 63 over the positions of wave t >> 6
-  const int d = lane, h2 = d >> 5, c = (d & 31) >> 2;
+  // thread t: feature t % 64 over the positions of wave t / 64
+  const int d = lane, pd = d / SDPL, c = (d % SDPL) / 4;
   float sum = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < 32; ++k)
-    sum += *reinterpret_cast<const __attribute__((address_space(3))) float*>(
-        wb + k * 256 + h2 * 128 + 16 * (c ^ (k & 7)) + 4 * (d & 3));
+#pragma unroll
+  for (int k = 0; k < SKPW; ++k)
+    sum += *(const lds_float*)(wb + k * 256 + pd * (4 * SDPL) + 16 * (c ^ (k % (SDPL / 4))) + 4 * (d % 4));
   __syncthreads();
-  float* red = reinterpret_cast<float*>(st0);  // [4][64]
+  lds_float* red = (lds_float*)(lds_char*)st0;  // [4][64]
   red[wave * HD + d] = sum;
   __syncthreads();
   if (tid < HD) *out = red[tid] + red[HD + tid] + red[2 * HD + tid] + red[3 * HD + tid];
@@ -954,11 +964,11 @@ DEV void fold_halves(const float (&acc)[32], char* st0, char* st1, float* out) {
 // key of the chunk (zero where the row does not attend: past it when causal,
 // or everywhere in an item without a global token) and the chunk's dQg
 // partial (unscaled), which bwd_gred sums.
-DEV void bwd_grow_stream(const BwdParams& p, int blk, char* st0, char* st1) {
+DEV void bwd_grow_stream(const BwdParams& p, int blk, char* st0) {
   constexpr int ROWB = ElemTraits<__bf16>::ROWB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hf = lane & 1, kl = lane >> 1;
+  const int part = lane % SLPK, kq = lane / SLPK;
   const int sp = blk % p.nsplit, bh = blk / p.nsplit;
   const int k_lo = sp * p.ksplit, k_end = min(p.n, k_lo + p.ksplit);
   const long base = (long)bh * p.n * ROWB;
@@ -966,58 +976,62 @@ DEV void bwd_grow_stream(const BwdParams& p, int blk, char* st0, char* st1) {
   const char* vgb = reinterpret_cast<const char*>(p.vg) + base;
   char* dkgb = reinterpret_cast<char*>(p.dkg) + base;
   char* dvgb = reinterpret_cast<char*>(p.dvg) + base;
-  const int nit = (k_end - k_lo + 127) / 128;
-  auto key = [&](int it) { return k_lo + 32 * (4 * it + wave) + kl; };
-  auto fetch = [&](int it, u32x4s (&kk)[4], u32x4s (&vv)[4]) {
+  const int nit = (k_end - k_lo + 4 * SKPW - 1) / (4 * SKPW);
+  auto key = [&](int it) { return k_lo + SKPW * (4 * it + wave) + kq; };
+  auto fetch = [&](int it, u32x4s (&kk)[SCH], u32x4s (&vv)[SCH]) {
     const long j = min(key(it), k_end - 1);
-    load_half(kk, kgb + j * ROWB, hf);
-    load_half(vv, vgb + j * ROWB, hf);
+    load_part(kk, kgb + j * ROWB, part);
+    load_part(vv, vgb + j * ROWB, part);
   };
-  u32x4s ka[4], va[4], kn[4], vn[4];
-  fetch(0, ka, va);
-  if (nit > 1) fetch(1, kn, vn);
+  u32x4s kbuf[SDEPTH][SCH], vbuf[SDEPTH][SCH];
+#pragma unroll
+  for (int s = 0; s < SDEPTH; ++s)
+    if (s < nit) fetch(s, kbuf[s], vbuf[s]);
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
   const bool has = gs.n > 0;  // workgroup-uniform
   const int pos = has ? gs.idx[0] : 0;
   const int k_att = !has ? k_lo : (p.causal ? min(k_end, pos + 1) : k_end);  // keys < k_att attend
-  u32x4s qg[4], dog[4];
+  u32x4s qg[SCH], dog[SCH];
   float lse2 = __builtin_inff(), dd = 0.f;
   if (has) {
-    load_half(qg, reinterpret_cast<const char*>(p.qg) + base + (long)pos * ROWB, hf);
-    load_half(dog, reinterpret_cast<const char*>(p.dout) + base + (long)pos * ROWB, hf);
+    load_part(qg, reinterpret_cast<const char*>(p.qg) + base + (long)pos * ROWB, part);
+    load_part(dog, reinterpret_cast<const char*>(p.dout) + base + (long)pos * ROWB, part);
     lse2 = p.glse2[(long)bh * p.ngp];
     dd = p.gdd[(long)bh * p.ngp];
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) { qg[c] = u32x4s{0u, 0u, 0u, 0u}; dog[c] = qg[c]; }
+    for (int c = 0; c < SCH; ++c) { qg[c] = u32x4s{0u, 0u, 0u, 0u}; dog[c] = qg[c]; }
   }
-  float dq[32];
+  float dq[SDPL];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) dq[i] = 0.f;
-  auto step = [&](int it, const u32x4s (&kk)[4], const u32x4s (&vv)[4]) {
+  for (int i = 0; i < SDPL; ++i) dq[i] = 0.f;
+  char* w2k = st0 + 2048 * wave;
+  auto step = [&](int it, const u32x4s (&kk)[SCH], const u32x4s (&vv)[SCH]) {
     const int j = key(it);
-    const float s = dot_pairs(qg, kk);
-    const float dp = dot_pairs(dog, vv);
+    const float s = dot_parts(qg, kk);
+    const float dp = dot_parts(dog, vv);
     const float pr = j < k_att ? __builtin_amdgcn_exp2f(s * p.c2 - lse2) : 0.f;
     const float ds = pr * (dp - dd);
-    axpy_half(dq, ds, kk);
-    u32x4s t[4];
-    scale_half(t, ds * p.scale, qg);
-    store_rows_nt(st0 + 4096 * wave, t, kl, hf, dkgb, j - kl, k_end);
-    scale_half(t, pr, dog);
-    store_rows_nt(st0 + 4096 * wave, t, kl, hf, dvgb, j - kl, k_end);
+    axpy_part(dq, ds, kk);
+    u32x4s t[SCH];
+    scale_part(t, ds * p.scale, qg);
+    store_rows_nt(w2k, t, kq, part, dkgb, j - kq, k_end);
+    scale_part(t, pr, dog);
+    store_rows_nt(w2k, t, kq, part, dvgb, j - kq, k_end);
   };
-  for (int it = 0; it < nit; it += 2) {
-    step(it, ka, va);
-    if (it + 2 < nit) fetch(it + 2, ka, va);
-    if (it + 1 < nit) {
-      step(it + 1, kn, vn);
-      if (it + 3 < nit) fetch(it + 3, kn, vn);
+  for (int it0 = 0; it0 < nit; it0 += SDEPTH) {
+#pragma unroll
+    for (int s = 0; s < SDEPTH; ++s) {
+      const int it = it0 + s;
+      if (it < nit) {
+        step(it, kbuf[s], vbuf[s]);
+        if (it + SDEPTH < nit) fetch(it + SDEPTH, kbuf[s], vbuf[s]);
+      }
     }
   }
   if (!has) return;  // workgroup-uniform: no dQg partial for an item without G
   float out = 0.f;
-  fold_halves(dq, st0, st1, &out);
+  fold_parts(dq, st0, &out);
   if (tid < HD) p.part_dqg[(((long)bh * p.ng + 0) * p.nsplit + sp) * HD + tid] = out;
 }
 
@@ -1025,11 +1039,11 @@ DEV void bwd_grow_stream(const BwdParams& p, int blk, char* st0, char* st1) {
 // dV[g] terms (unscaled dK) of the rows that attend to the global key g
 // from outside their band (rows of G have LSE +inf, so P = 0), one partial
 // per chunk for bwd_gred.
-DEV void bwd_gcol_stream(const BwdParams& p, int blk, char* st0, char* st1) {
+DEV void bwd_gcol_stream(const BwdParams& p, int blk, char* st0) {
   constexpr int ROWB = ElemTraits<__bf16>::ROWB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hf = lane & 1, kl = lane >> 1;
+  const int part = lane % SLPK, kq = lane / SLPK;
   const int ch = blk % p.nchunk, bh = blk / p.nchunk;
   const int qbeg = ch * p.gcol_qc, qend = min(p.n, qbeg + p.gcol_qc);
   const long base = (long)bh * p.n * ROWB;
@@ -1037,52 +1051,55 @@ DEV void bwd_gcol_stream(const BwdParams& p, int blk, char* st0, char* st1) {
   const char* db = reinterpret_cast<const char*>(p.dout) + base;
   const float* lse2 = p.lse2 + (long)bh * p.n;
   const float* ddr = p.dd + (long)bh * p.n;
-  const int nit = (qend - qbeg + 127) / 128;
-  auto row = [&](int it) { return qbeg + 32 * (4 * it + wave) + kl; };
-  auto fetch = [&](int it, u32x4s (&qq)[4], u32x4s (&oo)[4], float& l2, float& d) {
+  const int nit = (qend - qbeg + 4 * SKPW - 1) / (4 * SKPW);
+  auto row = [&](int it) { return qbeg + SKPW * (4 * it + wave) + kq; };
+  auto fetch = [&](int it, u32x4s (&qq)[SCH], u32x4s (&oo)[SCH], float& l2, float& d) {
     const long i = min(row(it), qend - 1);
-    load_half(qq, qb + i * ROWB, hf);
-    load_half(oo, db + i * ROWB, hf);
+    load_part(qq, qb + i * ROWB, part);
+    load_part(oo, db + i * ROWB, part);
     l2 = lse2[i];
     d = ddr[i];
   };
-  u32x4s qa[4], oa[4], qn[4], on[4];
-  float la, da, ln, dn;
-  fetch(0, qa, oa, la, da);
-  if (nit > 1) fetch(1, qn, on, ln, dn);
+  u32x4s qbuf[SDEPTH][SCH], obuf[SDEPTH][SCH];
+  float lbuf[SDEPTH], dbuf[SDEPTH];
+#pragma unroll
+  for (int s = 0; s < SDEPTH; ++s)
+    if (s < nit) fetch(s, qbuf[s], obuf[s], lbuf[s], dbuf[s]);
   const GSet gs = batch_gset(p.gidx, p.goff, p.ng, bh / p.H);
   if (gs.n == 0) return;  // workgroup-uniform: no global key in this item
   const int gpos = gs.idx[0];
   const HeadGeom hg = p.heads[bh % p.H];
-  u32x4s kg[4], vg[4];
-  load_half(kg, reinterpret_cast<const char*>(p.k) + base + (long)gpos * ROWB, hf);
-  load_half(vg, reinterpret_cast<const char*>(p.v) + base + (long)gpos * ROWB, hf);
-  float dk[32], dv[32];
+  u32x4s kg[SCH], vg[SCH];
+  load_part(kg, reinterpret_cast<const char*>(p.k) + base + (long)gpos * ROWB, part);
+  load_part(vg, reinterpret_cast<const char*>(p.v) + base + (long)gpos * ROWB, part);
+  float dk[SDPL], dv[SDPL];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) { dk[i] = 0.f; dv[i] = 0.f; }
-  auto step = [&](int it, const u32x4s (&qq)[4], const u32x4s (&oo)[4], float l2, float d) {
+  for (int i = 0; i < SDPL; ++i) { dk[i] = 0.f; dv[i] = 0.f; }
+  auto step = [&](int it, const u32x4s (&qq)[SCH], const u32x4s (&oo)[SCH], float l2, float d) {
     const int i = row(it);
     const int dl = i - gpos;  // the row holds g in its band iff g is a band key of it
     const bool inband = dl >= -hg.right * hg.dil && dl <= hg.half * hg.dil && dl % hg.dil == 0;
     const bool ok = i < qend && !inband && !(p.causal && gpos > i);
-    const float s = dot_pairs(qq, kg);
-    const float dp = dot_pairs(oo, vg);
+    const float s = dot_parts(qq, kg);
+    const float dp = dot_parts(oo, vg);
     const float pr = ok ? __builtin_amdgcn_exp2f(s * p.c2 - l2) : 0.f;  // l2 = +inf on rows of G
     const float ds = pr * (dp - d);
-    axpy_half(dk, ds, qq);
-    axpy_half(dv, pr, oo);
+    axpy_part(dk, ds, qq);
+    axpy_part(dv, pr, oo);
   };
-  for (int it = 0; it < nit; it += 2) {
-    step(it, qa, oa, la, da);
-    if (it + 2 < nit) fetch(it + 2, qa, oa, la, da);
-    if (it + 1 < nit) {
-      step(it + 1, qn, on, ln, dn);
-      if (it + 3 < nit) fetch(it + 3, qn, on, ln, dn);
+  for (int it0 = 0; it0 < nit; it0 += SDEPTH) {
+#pragma unroll
+    for (int s = 0; s < SDEPTH; ++s) {
+      const int it = it0 + s;
+      if (it < nit) {
+        step(it, qbuf[s], obuf[s], lbuf[s], dbuf[s]);
+        if (it + SDEPTH < nit) fetch(it + SDEPTH, qbuf[s], obuf[s], lbuf[s], dbuf[s]);
+      }
     }
   }
   float outk = 0.f, outv = 0.f;
-  fold_halves(dk, st0, st1, &outk);
-  fold_halves(dv, st0, st1, &outv);
+  fold_parts(dk, st0, &outk);
+  fold_parts(dv, st0, &outv);
   if (tid < HD) {
     float* rec = p.part_gkv + (((long)bh * p.nchunk + ch) * p.ng32 + 0) * (2 * HD);
     rec[tid] = outk;
@@ -1146,13 +1163,13 @@ __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
   __shared__ int gmeta[2][KT];
   int b = blockIdx.x;
   if (b < p.n_gcol) {
-    if constexpr (GSTREAM) bwd_gcol_stream(p, b, st0, st1);
+    if constexpr (GSTREAM) bwd_gcol_stream(p, b, st0);
     else bwd_gcol_block(p, b, st0, st1, st2);
     return;
   }
   b -= p.n_gcol;
   if (b < p.n_gq) {
-    if constexpr (GSTREAM) bwd_grow_stream(p, b, st0, st1);
+    if constexpr (GSTREAM) bwd_grow_stream(p, b, st0);
     else bwd_gq_block(p, b, st0, st1, st2);
     return;
   }
