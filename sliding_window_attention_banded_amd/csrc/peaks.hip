@@ -4,7 +4,10 @@
 //     per wave): once with constant operands and once with random ones, since
 //     the sustained clock depends on how much the operands toggle;
 //   * LDS read bandwidth (conflict-free ds_read_b128 streams) per CU;
-//   * HBM copy bandwidth (16 bytes per lane, a 1 GiB buffer each way).
+//   * HBM bandwidth on 1 GiB buffers: a plain copy (16 bytes per lane per
+//     step), a copy with four 16-byte loads in flight per lane and
+//     non-temporal stores, a read-only stream (summed, so the loads stay) and
+//     a write-only stream of non-temporal stores.
 // The shader clock is measured from s_memtime against the 100 MHz
 // s_memrealtime counter on one wave. Prints one line per probe.
 #include <hip/hip_runtime.h>
@@ -81,6 +84,40 @@ __global__ __launch_bounds__(512) void lds_probe(unsigned* out, int iters, unsig
 
 __global__ __launch_bounds__(256) void copy_probe(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = src[i];
+}
+
+// four 16-byte loads in flight per lane, then four non-temporal stores; n is
+// a multiple of 4 * 256 * gridDim.x
+__global__ __launch_bounds__(256) void copy4_probe(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(v[k], dst + i + k * stride);
+  }
+}
+
+// read-only: four loads in flight per lane, summed; one word per lane out
+__global__ __launch_bounds__(256) void read_probe(const u32x4* __restrict__ src, unsigned* out, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  unsigned acc = 0;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// write-only: non-temporal 16-byte stores
+__global__ __launch_bounds__(256) void write_probe(u32x4* __restrict__ dst, size_t n) {
+  const u32x4 v{1u, 2u, 3u, 4u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    __builtin_nontemporal_store(v, dst + i);
 }
 
 float time_ms(hipEvent_t e0, hipEvent_t e1) {
@@ -172,6 +209,38 @@ int main() {
     }
     std::printf("hbm_copy  1 GiB    %8.1f GB/s   (read + write bytes over the best of 5 copies)\n",
                 2.0 * bytes / (best * 1e-3) / 1e9);
+    // the other streams, best of 5 each; the grid divides n evenly
+    unsigned* sink;
+    CHECK(hipMalloc(&sink, sizeof(unsigned) * 256 * (size_t)blocks));
+    auto best_of = [&](auto launch) {
+      launch();
+      CHECK(hipDeviceSynchronize());
+      float b = 1e30f;
+      for (int rep = 0; rep < 5; ++rep) {
+        CHECK(hipEventRecord(e0));
+        launch();
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        CHECK(hipGetLastError());
+        const float ms = time_ms(e0, e1);
+        if (ms < b) b = ms;
+      }
+      return b;
+    };
+    if (n % (4 * 256 * (size_t)blocks) != 0) {
+      std::fprintf(stderr, "grid does not divide the buffer\n");
+      std::exit(1);
+    }
+    const float t4 = best_of([&] { hipLaunchKernelGGL(copy4_probe, dim3(blocks), dim3(256), 0, 0, src, dst, n); });
+    std::printf("hbm_copy4 1 GiB    %8.1f GB/s   (4 loads in flight per lane, non-temporal stores)\n",
+                2.0 * bytes / (t4 * 1e-3) / 1e9);
+    const float tr = best_of([&] { hipLaunchKernelGGL(read_probe, dim3(blocks), dim3(256), 0, 0, src, sink, n); });
+    std::printf("hbm_read  1 GiB    %8.1f GB/s   (read only, 4 loads in flight per lane)\n",
+                1.0 * bytes / (tr * 1e-3) / 1e9);
+    const float tw = best_of([&] { hipLaunchKernelGGL(write_probe, dim3(blocks), dim3(256), 0, 0, dst, n); });
+    std::printf("hbm_write 1 GiB    %8.1f GB/s   (write only, non-temporal stores)\n",
+                1.0 * bytes / (tw * 1e-3) / 1e9);
+    CHECK(hipFree(sink));
     CHECK(hipFree(src));
     CHECK(hipFree(dst));
   }
