@@ -237,11 +237,11 @@ DEV void dq_ring_step(int tb, DqWave& w, const RingCtx& c, const Pol& pol, const
   const unsigned nxt = SN == 0 ? c.a0 : (SN == 1 ? c.a1 : c.a2);
   wait_vmcnt<Dma<__bf16>::PER_WAVE>();
   wg_barrier();
-  const int kn = c.kbeg + min(tb + 2, c.nband - 1) * KT;
+  const int kn = c.kbeg + ring_tile(c, min(tb + 2, c.nband - 1)) * KT;
   if (kn + KT <= c.kend) dma_tile_fast<__bf16>(nxt, dl, c.kb, c.vb, kn, c.r, c.dil, c.wave);
   else dma_tile<__bf16>(nxt, c.kb, c.vb, kn, c.kend, c.r, c.dil, c.wave, c.lane);
   if (!c.live) return;
-  const int k0 = c.kbeg + tb * KT;
+  const int k0 = c.kbeg + ring_tile(c, tb) * KT;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const int ku = k0 + 32 * kh;
@@ -294,6 +294,10 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
             (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
             wave, lane, g, wave_live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
+#ifndef SWATTN_BWD_NO_ROT
+  // neighbouring blocks start on the key tile they share, as in the forward
+  c.rot = band_rotation(q0, kbeg, nband, half, right);
+#endif
   const BandPol pol{qi, qw0, half, right, nr, max(0, qw0 - half), min(nr - 1, qw0 + 31 + right)};
 
   DqWave w;
@@ -472,12 +476,12 @@ DEV void dkv_ring_step(int tb, DkvWave& w, const RingCtx& c, const Pol& pol, con
   const unsigned nxt = SN == 0 ? c.a0 : (SN == 1 ? c.a1 : c.a2);
   wait_vmcnt<Dma<__bf16>::PER_WAVE + 1>();
   wg_barrier();
-  const int kn = c.kbeg + min(tb + 2, c.nband - 1) * KT;
+  const int kn = c.kbeg + ring_tile(c, min(tb + 2, c.nband - 1)) * KT;
   if (kn + KT <= c.kend) dma_tile_fast<__bf16>(nxt, dl, c.kb, c.vb, kn, c.r, c.dil, c.wave);
   else dma_tile<__bf16>(nxt, c.kb, c.vb, kn, c.kend, c.r, c.dil, c.wave, c.lane);
   dma_stats(nxt, lse2, dd, kn, c.kend, c.r, c.dil, c.wave, c.lane);
   if (!c.live) return;
-  const int k0 = c.kbeg + tb * KT;
+  const int k0 = c.kbeg + ring_tile(c, tb) * KT;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     const int ku = k0 + 32 * kh;
@@ -517,6 +521,10 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
             reinterpret_cast<const char*>(p.q) + base, reinterpret_cast<const char*>(p.dout) + base,
             qbeg, qend, nband, r, dil, wave, lane, g, wave_live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
+#ifndef SWATTN_BWD_NO_ROT
+  // neighbouring blocks start on the query tile they share
+  c.rot = band_rotation(k0, qbeg, nband, right, half);
+#endif
   const BandPol pol{kj, kw0, right, half, nr, max(0, kw0 - right), min(nr - 1, kw0 + 31 + half)};
   const float* lse2 = p.lse2 + (long)bh * p.n;
   const float* dd = p.dd + (long)bh * p.n;
@@ -525,9 +533,10 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
   acc2_zero(w.dk);
   acc2_zero(w.dv);
   const long roff = base + (long)pos_k * ROWB;
-  dma_tile<__bf16>(c.a0, c.kb, c.vb, qbeg, qend, r, dil, wave, lane);
-  dma_stats(c.a0, lse2, dd, qbeg, qend, r, dil, wave, lane);
-  const int q1 = qbeg + min(1, nband - 1) * KT;
+  const int q0t = qbeg + ring_tile(c, 0) * KT;
+  dma_tile<__bf16>(c.a0, c.kb, c.vb, q0t, qend, r, dil, wave, lane);
+  dma_stats(c.a0, lse2, dd, q0t, qend, r, dil, wave, lane);
+  const int q1 = qbeg + ring_tile(c, min(1, nband - 1)) * KT;
   dma_tile<__bf16>(c.a1, c.kb, c.vb, q1, qend, r, dil, wave, lane);
   dma_stats(c.a1, lse2, dd, q1, qend, r, dil, wave, lane);
   load_q(w.kf, reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(p.k) + roff), g);
