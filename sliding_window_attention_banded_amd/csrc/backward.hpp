@@ -294,10 +294,8 @@ DEV void bwd_dq_block(const BwdParams& p, int tile, char* st0, char* st1, char* 
             (unsigned)(uintptr_t)(lds_void*)st2, kb, vb, kbeg, kend, nband, r, dil,
             wave, lane, g, wave_live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
-#ifndef SWATTN_BWD_NO_ROT
   // neighbouring blocks start on the key tile they share, as in the forward
   c.rot = band_rotation(q0, kbeg, nband, half, right);
-#endif
   const BandPol pol{qi, qw0, half, right, nr, max(0, qw0 - half), min(nr - 1, qw0 + 31 + right)};
 
   DqWave w;
@@ -521,10 +519,8 @@ DEV void bwd_dkv_block(const BwdParams& p, int tile, char* st0, char* st1, char*
             reinterpret_cast<const char*>(p.q) + base, reinterpret_cast<const char*>(p.dout) + base,
             qbeg, qend, nband, r, dil, wave, lane, g, wave_live, p.c2, {}};
   lds_lanes_init(c.ll, lane);
-#ifndef SWATTN_BWD_NO_ROT
   // neighbouring blocks start on the query tile they share
   c.rot = band_rotation(k0, qbeg, nband, right, half);
-#endif
   const BandPol pol{kj, kw0, right, half, nr, max(0, kw0 - right), min(nr - 1, kw0 + 31 + half)};
   const float* lse2 = p.lse2 + (long)bh * p.n;
   const float* dd = p.dd + (long)bh * p.n;
