@@ -1183,9 +1183,14 @@ __global__ __launch_bounds__(256, 2) void bwd_main(BwdParams p) {
     if (b < p.n_gkv) { bwd_gkv_block(p, b, st0, st1, gmeta[0]); return; }
     b -= p.n_gkv;
   }
-  if (b < p.nq) { bwd_dq_block(p, xcd_remap(b, p.nq), st0, st1, st2, gmeta); return; }
-  b -= p.nq;
-  bwd_dkv_block(p, xcd_remap(b, p.nq), st0, st1, st2);
+  // The query and key blocks of a tile are neighbours in the order: a tile's
+  // K and V rows (the query blocks' ring tiles, the key block's own rows)
+  // and its Q and dO rows (the other way round) then meet in one XCD's L2 at
+  // about the same time, instead of being fetched once by the query blocks
+  // and again by the key blocks a round later.
+  const int lb = xcd_remap(b, 2 * p.nq);
+  if ((lb & 1) == 0) bwd_dq_block(p, lb >> 1, st0, st1, st2, gmeta);
+  else bwd_dkv_block(p, lb >> 1, st0, st1, st2);
 }
 
 }  // namespace swattn
