@@ -1422,54 +1422,62 @@ __global__ __launch_bounds__(256) void band_merge(BandParams p, long rows) {
 
 constexpr int MAX_SPLIT = 256;
 
-// Log-sum-exp merge of the key chunks of one global row; overwrites O and LSE.
-// One 256-thread block per (global row, b*h), grid = ng * B*H. Thread t owns
-// column t%64 of chunks t/64, t/64 + 4, ...; it loads them in batches of 8
-// (all loads of a batch in flight at once) and folds them into a running
-// (max, sum, output); the four groups are then folded the same way in LDS.
-
-// The partials' pointers and counts come first among the arguments so that
-// they can be preloaded into SGPRs (the build's kernarg-preload count): the
-// partial loads then go out as the waves start, together with the global
-// token's position, instead of after the argument fetch and the set lookup.
+// Log-sum-exp merge of the key chunks of the global rows; overwrites rows G
+// of O (and LSE). One wave per (b*h, global row), four rows per 256-thread
+// block, so that every wave of the grid is resident at once and the merge is
+// one memory round trip: lane d owns output column d and issues the loads of
+// up to 16 chunks' column d together with their (max, sum) records, which
+// are the same for every lane of the wave (scalar loads); the batch is folded
+// against its own maximum, and batches (rows of more than 16 chunks) into a
+// running (max, sum, output).
+//
+// The partials' pointers come first among the arguments so that they are
+// preloaded into SGPRs (the build's kernarg-preload count) and the loads go
+// out as the waves start.
 template <class T>
 __global__ __launch_bounds__(256) void global_rows_merge(const float* part_ml, const float* part_o,
-                                                         int ng, int nsplit, GlobalParams p) {
-  __shared__ float sm[4][HD], sl[4][HD], sa[4][HD];
-  const int gi = blockIdx.x % ng, bh = blockIdx.x / ng, tid = threadIdx.x;
-  const int d = tid & 63, grp = tid >> 6;
-  // in bounds for every (bh, gi < ng); used only when gi is a row of the item
-  const long slot0 = ((long)bh * ng + gi) * nsplit;
-  const float* ml = part_ml + slot0 * 2;
-  const float* po = part_o + slot0 * HD + d;
-  float M = -__builtin_inff(), L = 0.f, A = 0.f;
-  for (int b0 = grp; b0 < nsplit; b0 += 32) {
-    float m[8], l[8], o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int sidx = b0 + 4 * i;
-      const bool ok = sidx < nsplit;
-      m[i] = ok ? ml[2 * sidx] : -__builtin_inff();
-      l[i] = ok ? ml[2 * sidx + 1] : 0.f;
-      o[i] = ok ? po[(long)sidx * HD] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lse_fold(M, L, A, m[i], l[i], o[i], p.c2);
-  }
+                                                         int ng, int nsplit, int nrows, GlobalParams p) {
+  constexpr int NB = 16;  // chunks per batch
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), d = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;  // bh * ng + gi
+  if (row >= nrows) return;                // wave-uniform
+  const int bh = row / ng, gi = row - bh * ng;
   const GSet gs = batch_gset(p.gidx, p.goff, ng, bh / p.H);
-  if (gi >= gs.n) return;  // workgroup-uniform
-  const int pos = gs.idx[gi];
-  sm[grp][d] = M;
-  sl[grp][d] = L;
-  sa[grp][d] = A;
-  __syncthreads();
-  if (tid < HD) {
+  if (gi >= gs.n) return;  // not a row of this item's set
+  const float* ml = part_ml + (long)row * nsplit * 2;
+  const float* po = part_o + (long)row * nsplit * HD + d;
+  float M = -__builtin_inff(), L = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += NB) {
+    float m[NB], l[NB], o[NB];
 #pragma unroll
-    for (int q = 1; q < 4; ++q) lse_fold(M, L, A, sm[q][d], sl[q][d], sa[q][d], p.c2);
-    T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
-    orow[d] = (T)(A / L);
-    if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
+    for (int i = 0; i < NB; ++i) {
+      const bool ok = s0 + i < nsplit;  // wave-uniform
+      m[i] = ok ? ml[2 * (s0 + i)] : -__builtin_inff();
+      l[i] = ok ? ml[2 * (s0 + i) + 1] : 0.f;
+      o[i] = ok ? po[(long)(s0 + i) * HD] : 0.f;
+    }
+    float mb = M;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) mb = fmaxf(mb, m[i]);
+    // every chunk and the running state against the batch maximum (weights
+    // 0 for empty chunks, m = -inf; mb stays -inf only if everything so far
+    // is empty, and then L and A are 0)
+    const float fr = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((M - mb) * p.c2);
+    L *= fr;
+    A *= fr;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float w = m[i] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m[i] - mb) * p.c2);
+      L = __builtin_fmaf(l[i], w, L);
+      A = __builtin_fmaf(o[i], w, A);
+    }
+    M = mb;
   }
+  // the row attends at least to its own key, so L > 0
+  const int pos = gs.idx[gi];
+  T* orow = reinterpret_cast<T*>(p.o) + ((long)bh * p.n + pos) * HD;
+  orow[d] = (T)(A / L);
+  if (p.lse && d == 0) p.lse[(long)bh * p.n + pos] = M * p.scale + __logf(L);
 }
 
 }  // namespace swattn

@@ -512,9 +512,10 @@ int launch(swattn_plan* pl, const void* q, const void* k, const void* v, const v
     if (e != hipSuccess) return hip_fail(e, "launch band_merge");
   }
   if (pl->ng > 0 && !pl->gfuse) {
-    const dim3 mgrid(pl->ng * pl->B * pl->H);
+    const int nrows = pl->ng * pl->B * pl->H;  // <= B*H*n <= 2^31
+    const dim3 mgrid((unsigned)((nrows + 3) / 4));
     hipLaunchKernelGGL(global_rows_merge<T>, mgrid, block, 0, st, (const float*)gp.part_ml,
-                       (const float*)gp.part_o, gp.ng, gp.nsplit, gp);
+                       (const float*)gp.part_o, gp.ng, gp.nsplit, nrows, gp);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch global_rows_merge");
   }
