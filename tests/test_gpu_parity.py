@@ -149,6 +149,23 @@ def test_full_size_whole_slices(name, bh, kind):
     compare(one, o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ref_o, ref_lse, label=one.name)
 
 
+# Several global tokens in long sequences: the global rows' keys come in
+# more than 16 chunks (9000 keys in 256-key chunks: 36), so the merge folds
+# them in batches of 16 with a ragged last batch.
+LONG_G = [
+    W("long_globals", 1, 2, 9000, (64, 128), (1, 2), False, (0, 4500, 8999)),
+    W("long_globals_causal", 1, 2, 9000, (64, 128), (1, 2), True, (3, 4500, 8999)),
+    W("long_globals_fp32", 1, 1, 9000, 64, 1, False, (0, 8999), "fp32"),
+    W("long_globals_per_item", 2, 1, 9000, 64, 1, False, ((0, 8999), (4500,))),
+]
+
+
+@pytest.mark.parametrize("wl", LONG_G, ids=lambda w: w.name)
+@pytest.mark.parametrize("kind", ["normal", "sharp"])
+def test_long_sequence_global_rows(wl, kind):
+    _case(wl, 0, kind, rows=_sample_rows(wl))
+
+
 def test_full_size_headline_all_seeds():
     wl = WORKLOADS["encoder_b2_h12_n4096_w512_g1"]
     for seed in (1, 2):
