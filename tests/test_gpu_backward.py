@@ -122,6 +122,28 @@ def test_backward_full_size_slices(name, bh, kind):
                 rel=None if kind == "dedup" else 1e-2)
 
 
+# Long sequences with several global tokens: the global rows' gradients come
+# from many key chunks and the global columns' from many query chunks
+LONG_G_BWD = [
+    Workload("long_globals_bwd", 1, 2, 9000, 64, (64, 128), (1, 2), False, (0, 4500, 8999), "bf16", 0.125),
+    Workload("long_globals_bwd_causal", 1, 2, 9000, 64, (64, 128), (1, 2), True, (3, 4500, 8999), "bf16",
+             0.125),
+]
+
+
+@pytest.mark.parametrize("wl", LONG_G_BWD, ids=lambda w: w.name)
+@pytest.mark.parametrize("kind", ["normal", "dedup"])
+def test_backward_long_sequence_globals(wl, kind):
+    bh = [(0, 0), (0, 1)]
+    print(f"[bwd] {wl.name} slices {bh} kind={kind}", flush=True)
+    inp = make_inputs(wl, 0, kind)
+    dout = cotangent(wl, 0)
+    o, _, got = gpu_forward_backward(wl, inp, dout)
+    refs = _oracle_grads(wl, inp, dout, bh=bh)
+    check_grads(wl, inp, dout, o, got, refs, bh=bh, label=f"{wl.name}/{kind}",
+                rel=None if kind == "dedup" else 1e-2)
+
+
 def F(name, B, H, n, window, dilation, causal=False, G=()):
     win = (window,) * H if isinstance(window, int) else tuple(window)
     dil = (dilation,) * H if isinstance(dilation, int) else tuple(dilation)
