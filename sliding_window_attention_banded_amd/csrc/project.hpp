@@ -9,40 +9,50 @@
 // straight into out[p][b][h][i][0..63], the layout the attention reads, with
 // an optional bias added in fp32 before the bf16 rounding.
 //
-// Workgroup tile: 256 (or 128) tokens x 128 features, 4 waves as 2 x 2, each
-// wave 128 (64) tokens x 64 features = 4 (2) x 2 MFMA 32x32x16 tiles (PjCfg).
-// Both operands are read k-contiguous (W rows and x rows), 32 input features
-// per stage, through a 3-stage LDS ring filled by direct global->LDS loads,
-// so that two (three) workgroups share a CU and one's ring fill and stores
-// run under the others' MFMAs.
+// Workgroup tile: 256 tokens x 256 features, 8 waves as 2 x 4 (one workgroup
+// per CU), 256 tokens x 128 features, 4 waves as 2 x 2 (two per CU), or 128
+// tokens x 128 features, 4 waves as 2 x 2 (three per CU); each wave 128 (64)
+// tokens x 64 features = 4 (2) x 2 MFMA 32x32x16 tiles (PjCfg). Both operands are read k-contiguous (W rows and x rows), 32 input
+// features per stage, through a 3-stage LDS ring filled by direct
+// global->LDS loads, so that one wave's ring fill and stores run under the
+// other waves' MFMAs.
 #pragma once
 
 #include "kernels.hpp"
 
 namespace swattn {
 
-constexpr int PJ_TN = 128;                                 // output features per workgroup
+constexpr int PJ_TN = 128;                                 // features per tile when choosing the shape
 constexpr int PJ_TK = 32;                                  // input features per stage
 constexpr int PJ_ROWB = PJ_TK * 2;                         // bytes per staged row (bf16)
-constexpr int PJ_A_BYTES = PJ_TN * PJ_ROWB;                // W tile, 8 KB
-constexpr int PJ_A_NI = PJ_A_BYTES / 1024;                 // the first 8 loads fill the W tile
 constexpr int PJ_RPB = 1024 / PJ_ROWB;                     // rows per 1-KB load
 constexpr int PJ_GROUP = 4;                                // token tiles swept together
 
 // Workgroup shapes: TG 32-token groups per wave, so 2 * 32 * TG tokens per
-// workgroup. TG = 4: 256 tokens, a 72 KB ring, two workgroups per CU, fewer
-// operand bytes per MFMA (the encoder projection: 79 us against 88 us with
-// TG = 2). TG = 2: 128 tokens, a 48 KB ring, three per CU, for problems whose
-// 256-token tiles cannot give every CU two workgroups (1024 tokens: 9.4 us
-// against 13.9 us).
-template <int TG>
+// workgroup, and WN waves along 64 * WN output features. TG = 4, WN = 4: 256
+// tokens x 256 features, a 96 KB ring (128 KB of LDS with the staged output
+// tiles), one workgroup per CU: the W tile serves twice the tokens and the x
+// tile twice the features of the 4-wave shape, so fewer staged bytes per MFMA
+// (the encoder projection: 74 us against 78 us with 256 x 128 tiles of four
+// waves, two per CU, and 88 us with TG = 2), when the problem still has two
+// rounds of such workgroups; otherwise TG = 4, WN = 2, two per CU. TG = 2,
+// WN = 2: 128 tokens x 128 features, a 48 KB ring, three per CU, for problems
+// whose 256-token tiles cannot give every CU two workgroups (1024 tokens:
+// 9.4 us against 13.9 us).
+template <int TG, int WN = 2>
 struct PjCfg {
   static constexpr int WT = 32 * TG;                       // tokens per wave
   static constexpr int TM = 2 * WT;                        // tokens per workgroup
-  static constexpr int STAGE = PJ_A_BYTES + TM * PJ_ROWB;  // W + x tile per stage
+  static constexpr int TN = 64 * WN;                       // output features per workgroup
+  static constexpr int NW = 2 * WN;                        // waves: 2 along tokens, WN along features
+  static constexpr int A_BYTES = TN * PJ_ROWB;             // W tile
+  static constexpr int A_NI = A_BYTES / 1024;              // the first A_NI loads fill the W tile
+  static constexpr int STAGE = A_BYTES + TM * PJ_ROWB;     // W + x tile per stage
   static constexpr int NI = STAGE / 1024;                  // 1-KB loads per stage
-  static constexpr int PW = NI / 4;                        // loads per wave
-  static_assert(NI % 4 == 0, "loads split evenly over the four waves");
+  static constexpr int PW = NI / NW;                       // loads per wave
+  static constexpr int RING = 3 * STAGE;
+  static constexpr int LDS = RING > NW * WT * 128 ? RING : NW * WT * 128;  // ring, then the staged tiles
+  static_assert(NI % NW == 0, "loads split evenly over the waves");
 };
 
 struct ProjParams {
@@ -102,17 +112,17 @@ DEV void wait_lgkm0() {
   asm volatile("" ::: "memory");
 }
 
-template <int TG>
-__global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) {
-  using C = PjCfg<TG>;
-  __shared__ __attribute__((aligned(1024))) char lds[3 * C::STAGE];
+template <int TG, int WN = 2>
+__global__ __launch_bounds__(128 * WN, WN == 4 ? (TG == 4 ? 1 : 2) : (TG == 4 ? 2 : 3)) void proj_gemm(ProjParams p) {
+  using C = PjCfg<TG, WN>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   pj_tile(blockIdx.x, p, tm, tn);
-  const int tok0 = tm * C::TM, feat0 = tn * PJ_TN;
+  const int tok0 = tm * C::TM, feat0 = tn * C::TN;
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)lds;
   const unsigned rowbytes = (unsigned)p.D * 2u;
 
@@ -123,8 +133,8 @@ __global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) 
 #pragma unroll
   for (int i = 0; i < C::PW; ++i) {
     const int I = wave * C::PW + i;
-    const bool is_w = I < PJ_A_NI;
-    const int row = (is_w ? I : I - PJ_A_NI) * PJ_RPB + (lane >> 2);
+    const bool is_w = I < C::A_NI;
+    const int row = (is_w ? I : I - C::A_NI) * PJ_RPB + (lane >> 2);
     const int grow = is_w ? min(feat0 + row, p.N - 1) : min(tok0 + row, p.M - 1);
     doff[i] = (unsigned)grow * rowbytes + ((unsigned)pj_phys(row, lane & 3) << 4);
   }
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) 
 #pragma unroll
     for (int i = 0; i < C::PW; ++i) {
       const int I = wave * C::PW + i;
-      dma16_saddr(I < PJ_A_NI ? wb : xb, doff[i],
+      dma16_saddr(I < C::A_NI ? wb : xb, doff[i],
                   lds0 + (unsigned)(stage * C::STAGE + I * 1024));
     }
   };
@@ -145,9 +155,9 @@ __global__ __launch_bounds__(256, TG == 4 ? 2 : 3) void proj_gemm(ProjParams p) 
   int roff[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) roff[ks] = pj_off(lane & 31, 2 * ks + (lane >> 5));
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int a_off = wn * 64 * PJ_ROWB;                // this wave's 64 W rows
-  const int b_off = PJ_A_BYTES + wm * C::WT * PJ_ROWB;  // this wave's x rows
+  const int b_off = C::A_BYTES + wm * C::WT * PJ_ROWB;  // this wave's x rows
 
   // This wave's 64 output features are one (projection, head) block; its
   // bias is read before the main loop so that the load's latency is hidden.

@@ -825,8 +825,15 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
       cus = 256;
   }
   const int tg = proj_choose_tg(M, N, cus);  // workgroup shape (PjCfg)
-  const long tm_tokens = 64L * tg;
-  const long ntm = (M + tm_tokens - 1) / tm_tokens, ntn = (N + PJ_TN - 1) / PJ_TN;
+  // 256-token workgroups: eight waves over 256 output features (one per CU),
+  // whose staged W and x tiles serve twice the MFMA work of four waves over
+  // 128 features, when that still gives at least two rounds of workgroups
+  // (the encoder's and LED's six projections: 78 -> 74 us, 155 -> 141 us);
+  // otherwise, and for 128-token workgroups, four waves over 128 features
+  const long ntm4 = (M + 255) / 256, ntn4 = (N + 255) / 256;
+  const int wn = tg == 4 && ntm4 * ntn4 >= 2L * cus ? 4 : 2;  // waves along the output features
+  const long tm_tokens = 64L * tg, tn_feats = 64L * wn;
+  const long ntm = (M + tm_tokens - 1) / tm_tokens, ntn = (N + tn_feats - 1) / tn_feats;
   if (ntm * ntn > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
   ProjParams pp;
   pp.x = static_cast<const __bf16*>(x);
@@ -835,7 +842,10 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   pp.out = static_cast<__bf16*>(out);
   pp.M = (int)M; pp.N = (int)N; pp.D = d_model; pp.n = n; pp.B = batch; pp.H = heads;
   pp.tg = tg; pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn);
-  if (tg == 4)
+  if (tg == 4 && wn == 4)
+    hipLaunchKernelGGL((proj_gemm<4, 4>), dim3((unsigned)pp.nblocks), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), pp);
+  else if (tg == 4)
     hipLaunchKernelGGL(proj_gemm<4>, dim3((unsigned)pp.nblocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), pp);
   else

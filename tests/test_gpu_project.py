@@ -78,6 +78,7 @@ def test_project_small(B, n, D, H, P, bias):
     (2, 4096, 768, 12, 6),    # Longformer-base encoder layer, local + global projections
     (1, 16384, 768, 12, 6),   # LED encoder layer at 16K tokens
     (4, 4096, 768, 12, 3),    # QA batch, local projections only
+    (2, 4096, 768, 12, 3),    # encoder layer without global tokens (256 x 128 workgroup tiles)
 ])
 def test_project_full_size(B, n, D, H, P):
     from sliding_window_attention_banded_amd import project
