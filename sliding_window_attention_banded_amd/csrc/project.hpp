@@ -68,6 +68,7 @@ struct ProjParams {
   int H;
   int tg;              // workgroup shape (PjCfg)
   int ntm;             // ceil(M / (64 * tg))
+  int feat_base;       // first output feature of this launch
   int ntn;             // ceil(N / 128)
   int nblocks;         // ntm * ntn
 };
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(128 * WN, WN == 4 ? (TG == 4 ? 1 : 2) : (TG == 4 ? 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int tm, tn;
   pj_tile(blockIdx.x, p, tm, tn);
-  const int tok0 = tm * C::TM, feat0 = tn * C::TN;
+  const int tok0 = tm * C::TM, feat0 = p.feat_base + tn * C::TN;
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_void*)lds;
   const unsigned rowbytes = (unsigned)p.D * 2u;
 

@@ -833,24 +833,44 @@ extern "C" int swattn_project(const void* x, const void* w, const void* bias, vo
   const long ntm4 = (M + 255) / 256, ntn4 = (N + 255) / 256;
   const int wn = tg == 4 && ntm4 * ntn4 >= 2L * cus ? 4 : 2;  // waves along the output features
   const long tm_tokens = 64L * tg, tn_feats = 64L * wn;
-  const long ntm = (M + tm_tokens - 1) / tm_tokens, ntn = (N + tn_feats - 1) / tn_feats;
-  if (ntm * ntn > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+  const long ntm = (M + tm_tokens - 1) / tm_tokens, ntn_all = (N + tn_feats - 1) / tn_feats;
+  if (ntm * ntn_all > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+  // With eight-wave tiles (one workgroup per CU) and a last round at most a
+  // third full, the feature tiles past the last whole round go to a second
+  // launch of 128 x 128 tiles, four times as many workgroups for their work,
+  // so that the last round is not a few CUs running whole tiles (the
+  // encoder's six projections, a quarter-full third round: 72.6-72.9 ->
+  // 69.5-69.9 us; LED's, a half-full fifth round, ran 2.8 us slower split).
+  long ntn = ntn_all;
+  const long nt = ntm * ntn_all;
+  if (wn == 4 && nt > cus && nt % cus != 0 && 3 * (nt % cus) <= cus) {
+    const long whole = nt / cus * cus / ntm;  // feature tiles filling whole rounds
+    if (whole >= 1) ntn = whole;
+  }
   ProjParams pp;
   pp.x = static_cast<const __bf16*>(x);
   pp.w = static_cast<const __bf16*>(w);
   pp.bias = static_cast<const __bf16*>(bias);
   pp.out = static_cast<__bf16*>(out);
   pp.M = (int)M; pp.N = (int)N; pp.D = d_model; pp.n = n; pp.B = batch; pp.H = heads;
-  pp.tg = tg; pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn);
+  pp.tg = tg; pp.ntm = (int)ntm; pp.ntn = (int)ntn; pp.nblocks = (int)(ntm * ntn); pp.feat_base = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   if (tg == 4 && wn == 4)
-    hipLaunchKernelGGL((proj_gemm<4, 4>), dim3((unsigned)pp.nblocks), dim3(512), 0,
-                       static_cast<hipStream_t>(stream), pp);
+    hipLaunchKernelGGL((proj_gemm<4, 4>), dim3((unsigned)pp.nblocks), dim3(512), 0, st, pp);
   else if (tg == 4)
-    hipLaunchKernelGGL(proj_gemm<4>, dim3((unsigned)pp.nblocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), pp);
+    hipLaunchKernelGGL(proj_gemm<4>, dim3((unsigned)pp.nblocks), dim3(256), 0, st, pp);
   else
-    hipLaunchKernelGGL(proj_gemm<2>, dim3((unsigned)pp.nblocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), pp);
+    hipLaunchKernelGGL(proj_gemm<2>, dim3((unsigned)pp.nblocks), dim3(256), 0, st, pp);
+  if (ntn < ntn_all) {
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return hip_fail(e0, "launch proj_gemm");
+    const long f0 = ntn * tn_feats;
+    const long ntm2 = (M + 127) / 128, ntn2 = (N - f0 + 127) / 128;
+    if (ntm2 * ntn2 > 0x7fffffffL) return fail(SWATTN_ERR_UNSUPPORTED, "too many blocks");
+    pp.tg = 2; pp.ntm = (int)ntm2; pp.ntn = (int)ntn2; pp.nblocks = (int)(ntm2 * ntn2);
+    pp.feat_base = (int)f0;
+    hipLaunchKernelGGL(proj_gemm<2>, dim3((unsigned)pp.nblocks), dim3(256), 0, st, pp);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch proj_gemm");
   return SWATTN_OK;
