@@ -1152,7 +1152,8 @@ __global__ __launch_bounds__(256) void bwd_gred(BwdParams p) {
 // ----------------------------------------------------------------------------
 // The main backward kernel: the global-token blocks first (global-column
 // partials, dQg partials, dKg/dVg), then the band query blocks (dq) and the
-// band key blocks (dk, dv) over the same tile schedule. The band blocks take
+// band key blocks (dk, dv) over the same tile schedule, the two blocks of a
+// tile next to each other. The band blocks take
 // several rounds of workgroup slots, so the long, mostly serial global-token
 // blocks start at once and the band blocks pack around them (on the encoder
 // workload 117.5 us instead of 133 us with them last).
