@@ -142,11 +142,6 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, long rows) {
 // ----------------------------------------------------------------------------
 // Shared pieces.
 
-// One 4-byte-per-lane global->LDS load (lane l lands at lds + 4 l).
-DEV void dma4(const void* src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
-               : "memory", "m0");
-}
 
 // A pair of fp32 accumulators for a 64-wide row block of 32 lanes (the same
 // layout as the forward's O^T accumulator).

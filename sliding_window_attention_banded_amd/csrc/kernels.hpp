@@ -889,6 +889,36 @@ DEV int band_rotation(int q0, int kbeg, int nband, int half, int right) {
   return min(t, nband - 1);
 }
 
+// One 4-byte-per-lane global->LDS load (lane l lands at lds + 4 l).
+DEV void dma4(const void* src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until this wave's LDS reads have returned (their registers are
+// written), so that a barrier after it also orders them before later
+// global->LDS loads into the same buffer.
+DEV void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  asm volatile("" ::: "memory");
+}
+
+// A band block's 128 query rows (residue-local q0 .., clamped to nr - 1) of
+// bf16 Q into a ring stage in the tiles' layout (row-major, 16-byte chunks
+// swizzled): wave w loads its own 32 rows, eight per 1 KB load.
+DEV void dma_qrows(unsigned stage, const char* qb, int q0, int nr, int r, int dil, int wave, int lane) {
+  constexpr int ROWB = ElemTraits<__bf16>::ROWB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + lane / 8;  // row of the block
+    const int pc = lane % 8;                       // the chunk slot this lane fills
+    const int kk = min(q0 + row, nr - 1);
+    dma16(qb + (long)(r + kk * dil) * ROWB + (ElemTraits<__bf16>::phys(row, pc) << 4),
+          stage + (unsigned)(1024 * (4 * wave + i)));
+  }
+}
+
 template <class T>
 DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st1, char* st2,
                     int (*gmeta)[KT]) {
@@ -956,22 +986,43 @@ DEV void band_block(const BandParams& p, int tile, int part, char* st0, char* st
 
   if constexpr (BF16) {
    if (ngb <= 1) {
-    // Band tiles 0 and 1, Q and (one global token) the key's K and V rows in
-    // one round trip; the global column is folded in from registers.
+    // One round trip for what the block starts with, every load a direct
+    // global->LDS one: the block's Q rows into stage 2 (free until ring step
+    // 0 refills it), with one global token its K and V rows into the
+    // global-column metadata's space (unused then), band tiles 0 and 1. The
+    // block waits for all but tile 1, so that its first tile's compute runs
+    // while tile 1 lands; Q and the global key then go to registers, and the
+    // global column is folded in from there.
     QFrag<T> kgf;
     bf16x4 vgr[2][4];
-    if (c.nband > 0) ring_start<T>(c);
-    load_q(qf, qrow, g);
+    char* kgrow = reinterpret_cast<char*>(&gmeta[0][0]);  // K row (128 B), then V row
+    dma_qrows(c.a2, reinterpret_cast<const char*>(p.q) + base, q0, nr, r, dil, wave, lane);
+    if (ngb == 1 && wave == 0)
+      dma4((lane < 32 ? kb : vb) + (long)gpos1 * ROWB + 4 * (lane & 31),
+           (unsigned)(uintptr_t)(lds_void*)kgrow);
+    if (c.nband > 0) {
+      ring_start<T>(c);
+      wait_vmcnt<Dma<T>::PER_WAVE>();  // everything but tile 1
+    } else {
+      wait_vmcnt<0>();
+    }
+    wg_barrier();  // every wave's rows of Q, the global key and tile 0 have landed
+    {
+      const int row = 32 * wave + (lane & 31);  // this lane's query row in the block
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        qf.v[st] = *reinterpret_cast<const bf16x8*>(st2 + ElemTraits<__bf16>::lds_off(row, 2 * st + g));
+    }
     if (ngb == 1) {
-      const T* krow = reinterpret_cast<const T*>(kb + (long)gpos1 * ROWB);
-      const T* vrow = reinterpret_cast<const T*>(vb + (long)gpos1 * ROWB);
-      load_q(kgf, krow, g);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) kgf.v[st] = *reinterpret_cast<const bf16x8*>(kgrow + 16 * (2 * st + g));
 #pragma unroll
       for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) vgr[dh][a] = *reinterpret_cast<const bf16x4*>(vrow + 32 * dh + 8 * a + 4 * g);
+        for (int a = 0; a < 4; ++a)
+          vgr[dh][a] = *reinterpret_cast<const bf16x4*>(kgrow + ROWB + 2 * (32 * dh + 8 * a + 4 * g));
     }
-    wait_vmcnt<0>();
+    wait_lgkm0();  // the reads of stage 2 are done before ring step 0 refills it
     if (ngb == 1 && wave_live) {
       // the key counts for this row if it is left of the row when causal and
       // not already in the row's band

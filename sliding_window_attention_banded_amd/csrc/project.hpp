@@ -104,14 +104,6 @@ inline int proj_choose_tg(long M, long N, int cus) {
   return big_tiles < 2L * cus ? 2 : 4;
 }
 
-// Wait until this wave's LDS reads have returned (their registers are
-// written), so that a barrier after it also orders them before later
-// global->LDS loads into the same buffer.
-DEV void wait_lgkm0() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
-  asm volatile("" ::: "memory");
-}
 
 template <int TG, int WN = 2>
 __global__ __launch_bounds__(128 * WN, WN == 4 ? (TG == 4 ? 1 : 2) : (TG == 4 ? 2 : 3)) void proj_gemm(ProjParams p) {
